@@ -1,0 +1,211 @@
+"""Float64 reference arithmetic (test infrastructure only; see package docstring).
+
+Notation follows the Slim Attention article (localbendi.com), section
+"K-Cache is All You Need": row-vector convention, Q = X.W_Q, K = X.W_K,
+V = X.W_V; W_KV = W_K^-1 . W_V; V = K . W_KV.  A head h owns the columns
+[h*dh, (h+1)*dh) of q, K and V.  Scores are scaled by ``scale`` (1/sqrt(dh)
+for standard MHA, which the pages leave implicit).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (round to nearest even) -> bfloat16 (round to nearest
+    even), returned as float64 values."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    keep = u >> np.uint64(16)
+    rest = u & np.uint64(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))
+    keep = keep + up.astype(np.uint64)
+    out = (keep << np.uint64(16)).astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isfinite(f), out, f.astype(np.float64))
+
+
+def cache_to_f64(K: np.ndarray) -> np.ndarray:
+    """A cache in storage dtype (float32, or uint16 bf16 bits) as float64."""
+    if K.dtype == np.uint16:
+        return bf16_decode(K)
+    return np.asarray(K, dtype=np.float64)
+
+
+def _clamp_len(n, T):
+    return int(min(max(int(n), 0), T))
+
+
+# ----------------------------------------------------------------------------
+# standard MHA decode: the definition the GPU path must reproduce
+
+def mha_decode(q, K, V, lengths, H: int, dh: int, scale: float) -> np.ndarray:
+    """Standard multi-head attention for one new query per sequence.
+
+    q [B, H*dh]; K, V [B, T, H*dh] (explicit caches); lengths [B].
+    Sequence b attends over its first len_b rows (clamped to [0, T]); a
+    sequence with no rows yields zeros.  Returns o [B, H, dh] float64.
+    For head h:  s_t = scale * q_h . K[t, h]   (the attention scores),
+    p = softmax(s),  o_h = sum_t p_t V[t, h]   (standard MHA, the baseline the
+    Slim Attention article rewrites).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, T = K.shape[0], K.shape[1]
+    o = np.zeros((B, H, dh))
+    for b in range(B):
+        n = _clamp_len(lengths[b], T)
+        if n == 0:
+            continue
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = scale * (K[b, :n, c] @ q[b, c])
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            o[b, h] = p @ V[b, :n, c]
+    return o
+
+
+def mha_decode_loop(q, K, V, lengths, H: int, dh: int, scale: float) -> np.ndarray:
+    """The same definition written as scalar loops (O(T*d) per sequence).
+    Only for tiny inputs; used to pin the matrix form above."""
+    B, T = len(K), len(K[0])
+    o = np.zeros((B, H, dh))
+    for b in range(B):
+        n = _clamp_len(lengths[b], T)
+        for h in range(H):
+            if n == 0:
+                continue
+            scores = []
+            for t in range(n):
+                acc = 0.0
+                for j in range(dh):
+                    acc += float(q[b][h * dh + j]) * float(K[b][t][h * dh + j])
+                scores.append(scale * acc)
+            m = max(scores)
+            weights = [math.exp(x - m) for x in scores]
+            z = sum(weights)
+            for j in range(dh):
+                num = 0.0
+                for t in range(n):
+                    num += weights[t] * float(V[b][t][h * dh + j])
+                o[b, h, j] = num / z
+    return o
+
+
+def explicit_values(K, W_K, W_V, cols=None, block: int = 8192) -> np.ndarray:
+    """Explicit value cache for a K cache, built without W_KV.
+
+    The K rows the device reads are K~ = round(X.W_K).  The context that
+    produced exactly these rows is X~ = K~ . W_K^-1 (float64 linear solve of
+    X~ W_K = K~), and its MHA value rows are V = X~ . W_V.  ``cols`` selects
+    columns of V (default: all).  K may be [T, d] or [B, T, d], in storage
+    dtype or float64; rows are processed in blocks of ``block``.
+    """
+    K = np.asarray(K)
+    W_K = np.asarray(W_K, dtype=np.float64)
+    W_V = np.asarray(W_V, dtype=np.float64)
+    Wv = W_V if cols is None else W_V[:, cols]
+    shape = K.shape
+    flat = K.reshape(-1, shape[-1])
+    out = np.empty((flat.shape[0], Wv.shape[1]))
+    WKt = W_K.T
+    for r0 in range(0, flat.shape[0], block):
+        r1 = min(flat.shape[0], r0 + block)
+        Kb = cache_to_f64(flat[r0:r1])
+        Xt = np.linalg.solve(WKt, Kb.T).T          # X~ W_K = K~
+        out[r0:r1] = Xt @ Wv
+    return out.reshape(shape[:-1] + (Wv.shape[1],))
+
+
+# ----------------------------------------------------------------------------
+# the Slim forms (pinned against the definition; not used as GPU reference)
+
+def wkv(W_K, W_V) -> np.ndarray:
+    """W_KV = W_K^-1 . W_V (Slim Attention article, section "K-Cache is All You
+    Need", the new parameter matrix), by float64 LU solve of W_K . W_KV = W_V."""
+    return np.linalg.solve(np.asarray(W_K, dtype=np.float64), np.asarray(W_V, dtype=np.float64))
+
+
+def slim_decode_opt1(q, K, W_KV, lengths, H: int, dh: int, scale: float) -> np.ndarray:
+    """Generation step, first option of the article: compute V = K . W_KV
+    from the K cache, then multiply the softmax result by V."""
+    K = cache_to_f64(np.asarray(K))
+    V = K @ np.asarray(W_KV, dtype=np.float64)
+    return mha_decode(q, K, V, lengths, H, dh, scale)
+
+
+def slim_decode_opt2(q, K, W_KV, lengths, H: int, dh: int, scale: float) -> np.ndarray:
+    """Generation step, second option of the article (better for long
+    sequences): multiply the softmax result by K first, then by W_KV.
+    Head h's value columns are K (all d columns) . W_KV[:, h*dh:(h+1)*dh], so
+    the softmax row of head h multiplies every column of K."""
+    q = np.asarray(q, dtype=np.float64)
+    K = cache_to_f64(np.asarray(K))
+    W_KV = np.asarray(W_KV, dtype=np.float64)
+    B, T = K.shape[0], K.shape[1]
+    o = np.zeros((B, H, dh))
+    for b in range(B):
+        n = _clamp_len(lengths[b], T)
+        if n == 0:
+            continue
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = scale * (K[b, :n, c] @ q[b, c])
+            e = np.exp(s - s.max())
+            p = e / e.sum()
+            u = p @ K[b, :n, :]                    # [d]
+            o[b, h] = u @ W_KV[:, c]
+    return o
+
+
+# ----------------------------------------------------------------------------
+# prompt phase: the K cache write
+
+def prefill(X, W_K, cache: str) -> np.ndarray:
+    """K = X . W_K in float64, rounded to the cache format ("f32": to float32;
+    "bf16": to float32 then bfloat16, both round-to-nearest-even).  The prompt
+    phase computes K for all tokens and caches it (article section "K-Cache is
+    All You Need", prompt phase).  X [..., d] and W_K [d, d] are taken as
+    float64 values of whatever the device is given."""
+    Kf = np.asarray(X, dtype=np.float64) @ np.asarray(W_K, dtype=np.float64)
+    if cache == "bf16":
+        return round_bf16(Kf)
+    return Kf.astype(np.float32).astype(np.float64)
+
+
+def prefill_loop(X, W_K, cache: str) -> np.ndarray:
+    """Scalar-loop form of ``prefill`` for tiny inputs."""
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W_K, dtype=np.float64)
+    n, d = X.shape
+    out = np.zeros((n, d))
+    for i in range(n):
+        for j in range(d):
+            acc = 0.0
+            for k in range(d):
+                acc += X[i, k] * W[k, j]
+            out[i, j] = acc
+    if cache == "bf16":
+        return round_bf16(out)
+    return out.astype(np.float32).astype(np.float64)
+
+
+def err_rel(o, o_ref) -> float:
+    """max |o - o_ref| / max |o_ref| over the whole output."""
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    den = np.abs(o_ref).max()
+    num = np.abs(o - o_ref).max()
+    return float(num / den) if den > 0 else float(num)

@@ -1,0 +1,339 @@
+"""Pins for the float64 oracle (CPU only).
+
+Every oracle function is checked against something other than itself: values
+worked by hand (tests/golden/hand_*.json), closed forms, scalar-loop brute
+force, textbook special cases and a library routine.  The planted-mistake
+tests at the end show that the pins catch the plausible slips (a dropped
+term, a wrong sign or index, a transposed operand).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+def _small_case(seed, B=2, T=9, H=2, dh=4, lens=None):
+    rng = np.random.default_rng(seed)
+    d = H * dh
+    q = rng.standard_normal((B, d))
+    K = rng.standard_normal((B, T, d))
+    V = rng.standard_normal((B, T, d))
+    if lens is None:
+        lens = rng.integers(1, T + 1, size=B)
+    return q, K, V, np.asarray(lens), H, dh, 1.0 / math.sqrt(dh)
+
+
+# ---------------------------------------------------------------------------
+# hand-derived values
+
+def test_hand_two_heads_all_forms():
+    g = _load("hand_two_heads.json")
+    q = np.array([g["q"]])
+    K = np.array([g["K"]])
+    V = np.array([g["V"]])
+    W = np.array(g["W_KV"])
+    o_ref = np.array([g["o"]])
+    lens = [2]
+    args = (g["H"], g["dh"], g["scale"])
+    assert np.abs(oracle.mha_decode(q, K, V, lens, *args) - o_ref).max() < 1e-14
+    assert np.abs(oracle.mha_decode_loop(q, K, V, lens, *args) - o_ref).max() < 1e-14
+    assert np.abs(oracle.slim_decode_opt1(q, K, W, lens, *args) - o_ref).max() < 1e-13
+    assert np.abs(oracle.slim_decode_opt2(q, K, W, lens, *args) - o_ref).max() < 1e-13
+    # V = K . W_KV, worked by hand
+    assert np.abs(K[0] @ W - V[0]).max() < 1e-14
+
+
+def test_hand_wkv_and_prefill():
+    g = _load("hand_wkv.json")
+    W_K, W_V = np.array(g["W_K"]), np.array(g["W_V"])
+    assert np.abs(oracle.wkv(W_K, W_V) - np.array(g["W_KV"])).max() < 1e-15
+    assert np.abs(np.linalg.inv(W_K) - np.array(g["W_K_inv"])).max() < 1e-15
+    X = np.array(g["X"])
+    assert np.abs(oracle.prefill(X, W_K, "f32") - np.array(g["K"])).max() == 0
+    assert np.abs(oracle.explicit_values(np.array(g["K"]), W_K, W_V) - np.array(g["V"])).max() < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# closed forms and the rewrite identity
+
+@pytest.mark.parametrize("name", ["c0", "c1"])
+def test_wkv_closed_form(name):
+    """W_K = Qo diag(s) Ro  =>  W_K^-1 = Ro^T diag(1/s) Qo^T, so
+    W_KV = Ro^T diag(1/s) Qo^T W_V exactly."""
+    cfg = syn.CONFIGS[name]
+    w = syn.weights(cfg)
+    closed = (w.Ro.T / w.s[None, :]) @ (w.Qo.T @ w.W_V)
+    assert _rel(oracle.wkv(w.W_K, w.W_V), closed) < 1e-12
+
+
+def test_eq2_rewrite_c0():
+    """V = X.W_V = (X.W_K).W_KV in float64 to 1e-10 (the identity of the
+    article's "K-Cache is All You Need" section)."""
+    cfg = syn.CONFIGS["c0"]
+    w = syn.weights(cfg)
+    X = syn.x_rows(cfg, 0, 0, cfg.T_max).astype(np.float64)
+    V = X @ w.W_V
+    V2 = (X @ w.W_K) @ oracle.wkv(w.W_K, w.W_V)
+    assert _rel(V2, V) < 1e-10
+
+
+def test_explicit_values_matches_unrounded_mha_c0():
+    """For an fp32 cache, X~ = K~ W_K^-1 recovers X to fp32 rounding and the
+    explicit V tracks X.W_V to the same order."""
+    cfg = syn.CONFIGS["c0"]
+    w = syn.weights(cfg)
+    lens = syn.lengths(cfg)
+    K = syn.k_cache(cfg, w, lens)
+    V = oracle.explicit_values(K, w.W_K, w.W_V)
+    X = syn.x_rows(cfg, 0, 0, cfg.T_max).astype(np.float64)
+    assert _rel(V[0], X @ w.W_V) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# brute force
+
+@pytest.mark.parametrize("seed,T,H,dh", [(1, 1, 1, 4), (2, 5, 2, 4), (3, 17, 4, 2), (4, 64, 2, 8)])
+def test_loop_vs_matrix(seed, T, H, dh):
+    q, K, V, lens, H, dh, scale = _small_case(seed, B=3, T=T, H=H, dh=dh)
+    a = oracle.mha_decode(q, K, V, lens, H, dh, scale)
+    b = oracle.mha_decode_loop(q, K, V, lens, H, dh, scale)
+    assert _rel(a, b) < 1e-12
+
+
+def test_loop_vs_matrix_c0():
+    cfg = syn.CONFIGS["c0"]
+    wl = syn.make(cfg)
+    K = oracle.cache_to_f64(wl.K)
+    V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
+    a = oracle.mha_decode(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
+    b = oracle.mha_decode_loop(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
+    assert _rel(a, b) < 1e-12
+
+
+def test_prefill_vs_loop():
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((3, 8))
+    W = rng.standard_normal((8, 8))
+    for cache in ("f32", "bf16"):
+        assert np.array_equal(oracle.prefill(X, W, cache), oracle.prefill_loop(X, W, cache))
+
+
+# ---------------------------------------------------------------------------
+# textbook special cases
+
+def test_len_one_returns_first_value_row():
+    q, K, V, _, H, dh, scale = _small_case(11, B=2, T=6, H=3, dh=4)
+    o = oracle.mha_decode(q, K, V, [1, 1], H, dh, scale)
+    assert np.abs(o - V[:, 0, :].reshape(2, H, dh)).max() < 1e-15
+
+
+def test_zero_query_is_mean_of_values():
+    q, K, V, _, H, dh, scale = _small_case(12, B=2, T=7, H=2, dh=4)
+    lens = [7, 3]
+    o = oracle.mha_decode(np.zeros_like(q), K, V, lens, H, dh, scale)
+    for b, n in enumerate(lens):
+        assert _rel(o[b], V[b, :n].mean(axis=0).reshape(H, dh)) < 1e-14
+
+
+def test_sharp_query_selects_row():
+    q, K, V, _, H, dh, scale = _small_case(13, B=1, T=8, H=2, dh=4)
+    for h in range(H):
+        c = slice(h * dh, (h + 1) * dh)
+        ts = int(np.argmax(np.linalg.norm(K[0, :, c], axis=1)))
+        q[0, c] = 1e4 * K[0, ts, c]
+        o = oracle.mha_decode(q, K, V, [8], H, dh, scale)
+        assert np.abs(o[0, h] - V[0, ts, c]).max() < 1e-9
+
+
+def test_permutation_invariance():
+    q, K, V, _, H, dh, scale = _small_case(14, B=1, T=10, H=2, dh=4)
+    perm = np.random.default_rng(0).permutation(10)
+    a = oracle.mha_decode(q, K, V, [10], H, dh, scale)
+    b = oracle.mha_decode(q, K[:, perm], V[:, perm], [10], H, dh, scale)
+    assert _rel(a, b) < 1e-13
+
+
+def test_duplicated_tokens_invariance():
+    q, K, V, _, H, dh, scale = _small_case(15, B=1, T=6, H=2, dh=4)
+    a = oracle.mha_decode(q, K, V, [6], H, dh, scale)
+    b = oracle.mha_decode(q, np.concatenate([K, K], 1), np.concatenate([V, V], 1), [12], H, dh, scale)
+    assert _rel(a, b) < 1e-13
+
+
+def test_linearity_in_values():
+    q, K, V, lens, H, dh, scale = _small_case(16, B=2, T=6, H=2, dh=4)
+    V2 = np.random.default_rng(1).standard_normal(V.shape)
+    a = oracle.mha_decode(q, K, V + 2.0 * V2, lens, H, dh, scale)
+    b = oracle.mha_decode(q, K, V, lens, H, dh, scale) + 2.0 * oracle.mha_decode(q, K, V2, lens, H, dh, scale)
+    assert _rel(a, b) < 1e-13
+
+
+def test_empty_and_clamped_lengths():
+    q, K, V, _, H, dh, scale = _small_case(17, B=2, T=5, H=2, dh=4)
+    o = oracle.mha_decode(q, K, V, [0, 99], H, dh, scale)
+    assert np.all(o[0] == 0)
+    assert _rel(o[1], oracle.mha_decode(q, K, V, [0, 5], H, dh, scale)[1]) == 0
+
+
+def test_identity_wk_gives_wv():
+    rng = np.random.default_rng(18)
+    W_V = rng.standard_normal((6, 6))
+    assert np.array_equal(oracle.wkv(np.eye(6), W_V), W_V)
+
+
+# ---------------------------------------------------------------------------
+# the Slim forms agree with explicit-V MHA
+
+@pytest.mark.parametrize("name,T,B", [("c0", None, None), ("c1", 64, 2)])
+def test_opt1_opt2_explicit_agree(name, T, B):
+    cfg = syn.CONFIGS[name]
+    if T is not None:
+        cfg = syn.shrink(cfg, T_max=T, B=B)
+    wl = syn.make(cfg)
+    K = oracle.cache_to_f64(wl.K)
+    V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
+    W = oracle.wkv(wl.w.W_K, wl.w.W_V)
+    args = (wl.lengths, cfg.H, cfg.dh, cfg.scale)
+    ref = oracle.mha_decode(wl.q, K, V, *args)
+    assert _rel(oracle.slim_decode_opt1(wl.q, wl.K, W, *args), ref) < 1e-10
+    assert _rel(oracle.slim_decode_opt2(wl.q, wl.K, W, *args), ref) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# storage formats, pinned to a library routine
+
+def test_round_bf16_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(19)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+        # exact bf16 ties (lower 16 bits 0x8000) with even and odd kept bits
+        (np.arange(1, 2001, dtype=np.uint32) << 16 | 0x8000).view(np.float32).astype(np.float64),
+        np.array([0.0, -0.0, 1.0, -1.5, 3.0e38, -3.0e38]),
+    ])
+    ours = oracle.round_bf16(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+    # the generator's storage rounding follows the same rule
+    bits = syn.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(oracle.bf16_decode(bits), ref)
+
+
+def test_generator_row_blocks_are_stable():
+    cfg = syn.shrink(syn.CONFIGS["c1"], T_max=3000, B=1)
+    a = syn.x_rows(cfg, 0, 0, 3000)
+    b = syn.x_rows(cfg, 0, 500, 2100)
+    c = syn.x_rows(cfg, 0, 0, 700)
+    assert np.array_equal(a[500:2100], b)
+    assert np.array_equal(a[:700], c)
+
+
+def test_generator_wk_conditioning():
+    for name in ("c0", "c1", "c4"):
+        w = syn.weights(syn.CONFIGS[name])
+        assert np.linalg.cond(w.W_K) <= 4.0 * 1.01
+
+
+def test_memory_halving():
+    """K-only cache bytes are exactly half of K+V cache bytes at equal dtype
+    (the article's 2x context-memory claim)."""
+    for cfg in syn.CONFIGS.values():
+        per = 4 if cfg.cache == "f32" else 2
+        k_only = cfg.B * cfg.T_max * cfg.d * per
+        kv = 2 * cfg.B * cfg.T_max * cfg.d * per
+        assert k_only * 2 == kv
+
+
+def test_golden_c0_regression():
+    """Guards the oracle against drift: output written by
+    tests/golden/make_golden.py (which calls only oracle/ and synthetic/)."""
+    g = _load("c0_oracle.json")
+    cfg = syn.CONFIGS["c0"]
+    wl = syn.make(cfg)
+    K = oracle.cache_to_f64(wl.K)
+    V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
+    o = oracle.mha_decode(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
+    assert _rel(o, np.array(g["o"])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each mutant of the decode definition must fail a pin
+
+def _mut_no_scale(q, K, V, lens, H, dh, scale):
+    return oracle.mha_decode(q, K, V, lens, H, dh, 1.0)
+
+
+def _mut_no_normalise(q, K, V, lens, H, dh, scale):
+    B, T = K.shape[:2]
+    o = np.zeros((B, H, dh))
+    for b in range(B):
+        n = min(int(lens[b]), T)
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = scale * (K[b, :n, c] @ q[b, c])
+            o[b, h] = np.exp(s - s.max()) @ V[b, :n, c]
+    return o
+
+
+def _mut_wrong_value_head(q, K, V, lens, H, dh, scale):
+    V2 = np.roll(V.reshape(V.shape[0], V.shape[1], H, dh), 1, axis=2).reshape(V.shape)
+    return oracle.mha_decode(q, K, V2, lens, H, dh, scale)
+
+
+def _mut_sign(q, K, V, lens, H, dh, scale):
+    return oracle.mha_decode(-np.asarray(q), K, V, lens, H, dh, scale)
+
+
+def _mut_off_by_one(q, K, V, lens, H, dh, scale):
+    return oracle.mha_decode(q, K, V, np.maximum(np.asarray(lens) - 1, 1), H, dh, scale)
+
+
+def _mut_transposed_head_block(q, K, V, lens, H, dh, scale):
+    # scores from K with each head's block transposed (a common layout slip)
+    if dh == 1:
+        K2 = K[:, :, ::-1]
+    else:
+        K2 = K.reshape(K.shape[0], K.shape[1], H, dh)[..., ::-1].reshape(K.shape)
+    return oracle.mha_decode(q, K2, V, lens, H, dh, scale)
+
+
+def _pins_pass(f):
+    g = _load("hand_two_heads.json")
+    ok = np.abs(f(np.array([g["q"]]), np.array([g["K"]]), np.array([g["V"]]), [2],
+                  g["H"], g["dh"], g["scale"]) - np.array([g["o"]])).max() < 1e-12
+    for seed in (1, 2, 3):
+        q, K, V, lens, H, dh, scale = _small_case(seed, B=3, T=7, H=2, dh=4)
+        ok &= _rel(f(q, K, V, lens, H, dh, scale),
+                   oracle.mha_decode_loop(q, K, V, lens, H, dh, scale)) < 1e-12
+    return bool(ok)
+
+
+@pytest.mark.parametrize("mutant", [_mut_no_scale, _mut_no_normalise, _mut_wrong_value_head,
+                                    _mut_sign, _mut_off_by_one, _mut_transposed_head_block])
+def test_pins_catch_planted_mistakes(mutant):
+    assert _pins_pass(oracle.mha_decode)
+    assert not _pins_pass(mutant)
+
+
+def test_pins_catch_transposed_wkv():
+    g = _load("hand_two_heads.json")
+    args = (np.array([g["q"]]), np.array([g["K"]]), np.array(g["W_KV"]).T, [2], g["H"], g["dh"], g["scale"])
+    assert np.abs(oracle.slim_decode_opt2(*args) - np.array([g["o"]])).max() > 1e-3
