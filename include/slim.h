@@ -1,0 +1,200 @@
+/*
+ * slim.h -- C ABI of libslim.so: Slim-Attention K-cache-only decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (Slim Attention article, localbendi.com, section "K-Cache is
+ * All You Need"): in multi-head attention W_K and W_V are square; when W_K is
+ * invertible, W_KV = W_K^-1 . W_V is a new parameter matrix and the value
+ * rows follow from the key rows, V = X.W_V = X.W_K.W_K^-1.W_V = K.W_KV.  So
+ * only K is cached.  The prompt phase computes K for all tokens and caches
+ * it; each generation step computes the new query, its scores against the
+ * cached K and their softmax, and recovers V on the fly, either by forming
+ * V = K.W_KV and multiplying the softmax by it, or, better for long
+ * sequences, by multiplying the softmax by K first and the result by W_KV.
+ * This library implements the second form for the decode step.
+ *
+ * Conventions (all entry points):
+ *  - Row-vector convention (x.W).  d = H*dh.  Head h owns columns
+ *    [h*dh, (h+1)*dh) of q, K and the output.
+ *  - Every matrix is dense row-major with no padding.
+ *  - Device pointers are caller-owned device memory (e.g. torch tensors).
+ *    The library never allocates, frees or synchronises device memory or
+ *    streams; work is enqueued on `stream` (0 = the null stream) and the call
+ *    returns once it is enqueued.  Calls are re-entrant; calls that share a
+ *    workspace must not overlap.
+ *  - Argument checks run on the host before anything is enqueued; on an error
+ *    nothing is enqueued.  Device-resident values (lengths, t0) cannot be
+ *    checked on the host: they are clamped on the device as documented.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef SLIM_H
+#define SLIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLIM_OK = 0,
+  SLIM_ERR_INVALID = 1,      /* bad pointer, size, alignment or shape      */
+  SLIM_ERR_UNSUPPORTED = 2,  /* valid but not built (dtype pair, H, dh...) */
+  SLIM_ERR_WORKSPACE = 3,    /* workspace_bytes below the required size    */
+  SLIM_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  SLIM_ERR_SINGULAR = 5      /* W_K is singular to working precision       */
+} slim_status_t;
+
+typedef enum { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* slim_status_string(slim_status_t s);
+
+/*
+ * slim_wkv -- the new parameter matrix W_KV = W_K^-1 . W_V (article section
+ * "K-Cache is All You Need", first equation), computed once per layer on the
+ * host.
+ *   W_K, W_V : host, [d, d] float64, row-major.  W_K must be invertible.
+ *   W_KV_out : host, [d, d] in `out_dt` (float32 or bf16 bit patterns,
+ *              round-to-nearest-even from the float64 result).
+ * Method: LU factorisation of W_K with partial pivoting in float64, then
+ * forward and back substitution for the d right-hand sides W_V.  Multi-
+ * threaded on the host CPU (SLIM_HOST_THREADS overrides the thread count).
+ * Errors: SLIM_ERR_INVALID (null pointer, d <= 0), SLIM_ERR_UNSUPPORTED
+ * (out_dt), SLIM_ERR_SINGULAR (a zero pivot).  No HIP call is made.
+ */
+slim_status_t slim_wkv(const double* W_K, const double* W_V, int d,
+                       void* W_KV_out, slim_dtype_t out_dt);
+
+/*
+ * slim_prefill -- prompt phase / append: writes K rows into the cache
+ * (article section "K-Cache is All You Need": the prompt phase computes K for
+ * all input tokens in parallel and caches it instead of V; at the end of each
+ * generation step the new k is appended).
+ *   K_cache[b, t0[b] + i, :] = round(X[b, i, :] . W)   for i < n
+ *   X       : device, [B, n, d] in x_dt
+ *   W       : device, [d, d] in w_dt (W_K; any d x d projection works)
+ *   K_cache : device, [B, T_max, d] in k_dt
+ *   t0      : device int32 [B] start rows, or NULL for all zero.  Rows that
+ *             would land at or beyond T_max are not written.
+ * Supported dtype triples: (bf16, bf16, bf16) on MFMA with fp32 accumulation
+ * and round-to-nearest-even output, and (f32, f32, f32) in fp32.
+ * Errors: SLIM_ERR_INVALID (null X/W/K_cache, B, n, d or T_max <= 0,
+ * n > T_max, bf16 with d % 8 != 0 or pointers not 16-byte aligned),
+ * SLIM_ERR_UNSUPPORTED (other dtype triples), SLIM_ERR_HIP.
+ */
+slim_status_t slim_prefill(const void* X, slim_dtype_t x_dt,
+                           const void* W, slim_dtype_t w_dt,
+                           void* K_cache, slim_dtype_t k_dt,
+                           int B, int n, int d, int T_max,
+                           const int32_t* t0, hipStream_t stream);
+
+/*
+ * slim_decode_workspace_bytes -- device workspace slim_decode needs for this
+ * shape on the current device (it depends on the device's compute-unit
+ * count).  Returns 0 for shapes slim_decode rejects.
+ */
+size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t k_dt);
+
+/*
+ * slim_decode -- one generation step of Slim Attention for B sequences, one
+ * new query each (article section "K-Cache is All You Need", generation step,
+ * second option: softmax times K, then times W_KV).
+ *   q       : device float32 [B, d], the new queries (unscaled)
+ *   K_cache : device [B, T_max, d] in k_dt; sequence b reads rows [0, len_b)
+ *   lengths : device int32 [B]; len_b is clamped to [0, T_max]; len_b = 0
+ *             gives a zero output row.  Rows at or beyond len_b are never
+ *             read, whatever they hold.
+ *   W_KV    : device [d, d] in w_dt (from slim_wkv)
+ *   out     : device float32 [B, H, dh]:
+ *               out[b,h,:] = (softmax_t(scale * q_h . K[b,t,h-cols]) . K[b,:len_b,:])
+ *                            . W_KV[:, h*dh:(h+1)*dh]
+ *             which equals standard MHA with V = K . W_KV.
+ *   scale   : score scale, normally 1/sqrt(dh)
+ *   workspace, workspace_bytes : device scratch of at least
+ *             slim_decode_workspace_bytes(B, H, dh, T_max, k_dt) bytes,
+ *             16-byte aligned; its contents on entry do not matter.
+ * Arithmetic: scores, softmax and all accumulation in float32; for bf16 caches
+ * the softmax weights are rounded to bf16 for the MFMA contraction with K.
+ * Supported: k_dt bf16 (MFMA path: H <= 32, dh in {32, 64, 128}, d % 8 == 0)
+ * or f32 (H <= 64, any dh); w_dt f32 or bf16; B <= 4096.
+ * Errors: SLIM_ERR_INVALID (null pointers, B/H/dh/T_max <= 0, scale not
+ * finite, misaligned pointers), SLIM_ERR_UNSUPPORTED, SLIM_ERR_WORKSPACE,
+ * SLIM_ERR_HIP.
+ */
+slim_status_t slim_decode(const float* q,
+                          const void* K_cache, slim_dtype_t k_dt,
+                          const int32_t* lengths,
+                          const void* W_KV, slim_dtype_t w_dt,
+                          float* out,
+                          int B, int H, int dh, int T_max, float scale,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * slim_decode_attend / slim_decode_finish -- the two halves of slim_decode,
+ * for callers that schedule or time them separately.  Same arguments and
+ * checks as slim_decode; slim_decode is exactly attend followed by finish on
+ * the same stream with the same workspace.
+ *   attend : streams the K cache once; per token chunk: scores, online
+ *            softmax and the softmax-times-K contraction, leaving per-chunk
+ *            partial results (running max, normaliser, unnormalised
+ *            softmax.K row per head) in the workspace.
+ *   finish : merges the chunk partials of each sequence (log-sum-exp) and
+ *            applies W_KV per head, writing `out`.
+ */
+slim_status_t slim_decode_attend(const float* q,
+                                 const void* K_cache, slim_dtype_t k_dt,
+                                 const int32_t* lengths,
+                                 const void* W_KV, slim_dtype_t w_dt,
+                                 float* out,
+                                 int B, int H, int dh, int T_max, float scale,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+slim_status_t slim_decode_finish(const float* q,
+                                 const void* K_cache, slim_dtype_t k_dt,
+                                 const int32_t* lengths,
+                                 const void* W_KV, slim_dtype_t w_dt,
+                                 float* out,
+                                 int B, int H, int dh, int T_max, float scale,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * mha_decode_kv -- comparator: standard MHA decode over explicit K and V
+ * caches (the baseline the Slim Attention article halves), same conventions
+ * as slim_decode with V_cache [B, T_max, d] in kv_dt in place of W_KV:
+ *   out[b,h,:] = softmax_t(scale * q_h . K[b,t,h-cols]) . V[b,:len_b,h-cols]
+ * Supported: kv_dt bf16 (dh in {32, 64, 128}, d % 8 == 0).  Workspace from
+ * mha_decode_kv_workspace_bytes.
+ */
+size_t mha_decode_kv_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t kv_dt);
+slim_status_t mha_decode_kv(const float* q,
+                            const void* K_cache, const void* V_cache, slim_dtype_t kv_dt,
+                            const int32_t* lengths,
+                            float* out,
+                            int B, int H, int dh, int T_max, float scale,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * HBM probes (measurement only; not part of the method):
+ *   slim_probe_read : reads `bytes` from `src` with 16-byte loads and writes
+ *                     one float per workgroup to `sink` (device, at least
+ *                     slim_probe_sink_floats() floats); the achievable
+ *                     streaming-read rate of the device.
+ *   slim_probe_copy : copies `bytes` from `src` to `dst` (a plain copy kernel
+ *                     of known size, used to calibrate traffic counters).
+ * `bytes` must be a multiple of 16 and both pointers 16-byte aligned.
+ */
+int slim_probe_sink_floats(void);
+slim_status_t slim_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+slim_status_t slim_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLIM_H */

@@ -1,0 +1,71 @@
+// Host-side plan and launcher declarations shared by the libslim sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace slim {
+
+// Launch plan of one slim_decode call.  The token stream (all sequences'
+// live rows, concatenated) is cut into `nch` chunks; every chunk is handled
+// by `gc` workgroups, one per column group of `dc` columns of K.  Partial
+// results live in `nslots = nch + B - 1` slots of the workspace.
+struct DecodePlan {
+  bool bf16_k;     // MFMA path (bf16 cache) or fp32 VALU path
+  int gc;          // column groups
+  int dc;          // columns per group (multiple of 256 on the MFMA path)
+  int nw;          // waves per workgroup (MFMA path)
+  int nch;         // token chunks
+  int nslots;      // partial slots
+  int npc;         // W_KV row chunks of the projection
+  size_t off_U;    // [nslots, H, d] float
+  size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
+  size_t off_op;   // [npc, B, H, dh] float (per-row-chunk projection partials)
+  size_t bytes;
+};
+
+struct DecodeArgs {
+  const float* q;
+  const void* K;
+  const int32_t* lengths;
+  const void* W;
+  float* out;
+  int B, H, dh, d, T_max;
+  float scale;
+  bool w_bf16;
+  char* ws;
+};
+
+constexpr int kProjRows = 128;     // W_KV rows per projection workgroup
+constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
+constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)
+
+bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, DecodePlan* p);
+
+hipError_t launch_attend_bf16(const DecodePlan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_attend_f32(const DecodePlan& p, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_finish(const DecodePlan& p, const DecodeArgs& a, hipStream_t s);
+
+// comparator (explicit K and V caches)
+struct KVPlan {
+  int nch, nslots;
+  size_t off_o, off_ml, bytes;
+};
+bool make_kv_plan(int B, int H, int dh, int T_max, int ncu, KVPlan* p);
+hipError_t launch_mha_kv(const KVPlan& p, const float* q, const void* K, const void* V,
+                         const int32_t* lengths, float* out, int B, int H, int dh, int T_max,
+                         float scale, char* ws, hipStream_t s);
+
+hipError_t launch_prefill_bf16(const void* X, const void* W, void* Kc, int B, int n, int d,
+                               int T_max, const int32_t* t0, hipStream_t s);
+hipError_t launch_prefill_f32(const void* X, const void* W, void* Kc, int B, int n, int d,
+                              int T_max, const int32_t* t0, hipStream_t s);
+
+int probe_sink_floats();
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+int env_int(const char* name, int dflt);
+
+}  // namespace slim

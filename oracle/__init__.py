@@ -30,6 +30,7 @@ from .mha import (  # noqa: F401
     mha_decode,
     mha_decode_loop,
     explicit_values,
+    explicit_values_cols,
     wkv,
     slim_decode_opt1,
     slim_decode_opt2,

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/slim.h declares, rejects bad arguments on the host before any HIP
+call, and its host-side W_KV solver agrees with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def slim():
+    return pytest.importorskip("kv_cache_reduction_amd", reason="libslim.so not built")
+
+
+def _declared_functions():
+    txt = open(os.path.join(ROOT, "include", "slim.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)
+    keep = [n for n in names if n.startswith(("slim_", "mha_"))]
+    return sorted(set(keep))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("slim_wkv", "slim_prefill", "slim_decode", "slim_decode_attend", "slim_decode_finish",
+              "slim_decode_workspace_bytes", "mha_decode_kv", "mha_decode_kv_workspace_bytes",
+              "slim_status_string", "slim_probe_read", "slim_probe_copy", "slim_probe_sink_floats"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(slim):
+    for n in _declared_functions():
+        assert hasattr(slim.lib, n), f"{n} declared in include/slim.h but not exported"
+
+
+def test_status_strings(slim):
+    for code in range(6):
+        assert slim.lib.slim_status_string(code).decode() == slim.STATUS[code]
+
+
+# --- host-side argument checks: these return before any HIP call ----------
+
+def _decode_call(slim, fn, **over):
+    a = dict(q=1, K=16, kdt=slim.BF16, lens=4, W=16, wdt=slim.BF16, out=4, B=1, H=32, dh=128,
+             T=1024, scale=0.088, ws=256, wsb=1 << 20, stream=None)
+    a.update(over)
+    return fn(a["q"], a["K"], a["kdt"], a["lens"], a["W"], a["wdt"], a["out"], a["B"], a["H"],
+              a["dh"], a["T"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["slim_decode", "slim_decode_attend", "slim_decode_finish"])
+def test_decode_rejects_bad_arguments(slim, fn):
+    f = getattr(slim.lib, fn)
+    for field in ("q", "K", "lens", "W", "out", "ws"):
+        assert _decode_call(slim, f, **{field: None}) == 1, field
+    assert _decode_call(slim, f, B=0) == 1
+    assert _decode_call(slim, f, H=-1) == 1
+    assert _decode_call(slim, f, T=0) == 1
+    assert _decode_call(slim, f, scale=float("nan")) == 1
+    assert _decode_call(slim, f, K=24) == 1              # K cache not 16-byte aligned
+    assert _decode_call(slim, f, kdt=7) == 2              # unknown dtype
+    assert _decode_call(slim, f, wdt=9) == 2
+    assert _decode_call(slim, f, H=33) == 2               # MFMA path holds at most 32 heads
+    assert _decode_call(slim, f, dh=96) == 2
+    assert _decode_call(slim, f, B=5000) == 2
+    assert _decode_call(slim, f, kdt=slim.F32, dh=48, H=4) == 2  # fp32 path: dh a power of two
+
+
+def test_prefill_rejects_bad_arguments(slim):
+    f = slim.lib.slim_prefill
+    ok = dict(X=16, xd=slim.BF16, W=16, wd=slim.BF16, K=16, kd=slim.BF16, B=2, n=4, d=64, T=8, t0=None)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return f(a["X"], a["xd"], a["W"], a["wd"], a["K"], a["kd"], a["B"], a["n"], a["d"], a["T"],
+                 a["t0"], None)
+    assert call(X=None) == 1
+    assert call(K=None) == 1
+    assert call(n=9) == 1          # n > T_max
+    assert call(d=60) == 1         # bf16 rows must be 16-byte multiples
+    assert call(X=8) == 1          # misaligned
+    assert call(wd=slim.F32) == 2  # mixed dtypes are not built
+
+
+def test_comparator_rejects_bad_arguments(slim):
+    f = slim.lib.mha_decode_kv
+    assert f(None, 16, 16, slim.BF16, 4, 4, 1, 32, 128, 64, 0.1, 256, 1 << 20, None) == 1
+    assert f(1, 16, 16, slim.F32, 4, 4, 1, 32, 128, 64, 0.1, 256, 1 << 20, None) == 2
+    assert f(1, 16, 16, slim.BF16, 4, 4, 1, 40, 128, 64, 0.1, 256, 1 << 20, None) == 2
+
+
+def test_probes_reject_bad_arguments(slim):
+    assert slim.lib.slim_probe_read(None, 16, 16, None) == 1
+    assert slim.lib.slim_probe_read(16, 10, 16, None) == 1
+    assert slim.lib.slim_probe_copy(16, 16, 0, None) == 1
+
+
+# --- host W_KV solver ------------------------------------------------------
+
+def test_wkv_hand_example(slim):
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_wkv.json")))
+    W = slim.wkv(np.array(g["W_K"]), np.array(g["W_V"]), "f32")
+    assert np.array_equal(W, np.array(g["W_KV"], dtype=np.float32))
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c4"])
+def test_wkv_matches_oracle(slim, name):
+    w = syn.weights(syn.CONFIGS[name])
+    ref = oracle.wkv(w.W_K, w.W_V)
+    got32 = slim.wkv(w.W_K, w.W_V, "f32").astype(np.float64)
+    # float32 output: correctly rounded up to the LU's own float64 error
+    assert np.abs(got32 - ref).max() <= 2.0 ** -23 * np.abs(ref).max()
+    bits = slim.wkv(w.W_K, w.W_V, "bf16")
+    ref_bf = oracle.round_bf16(ref)
+    got_bf = oracle.bf16_decode(bits)
+    # round-to-nearest-even of the float64 result: equal except where the two
+    # float64 solves straddle a rounding boundary (then one bf16 ulp apart)
+    diff = got_bf != ref_bf
+    assert diff.mean() < 1e-3
+    ulp = np.abs(ref_bf) * 2.0 ** -7
+    assert np.all(np.abs(got_bf - ref_bf)[diff] <= ulp[diff] * 1.01)
+
+
+def test_wkv_general_matrix(slim):
+    rng = np.random.default_rng(3)
+    A = rng.standard_normal((200, 200))
+    Bm = rng.standard_normal((200, 200))
+    got = slim.wkv(A, Bm, "f32").astype(np.float64)
+    ref = np.linalg.solve(A, Bm)
+    assert np.abs(got - ref).max() / np.abs(ref).max() < 1e-5
+
+
+def test_wkv_singular(slim):
+    A = np.ones((8, 8))
+    with pytest.raises(slim.SlimError) as e:
+        slim.wkv(A, np.eye(8), "f32")
+    assert e.value.status == 5
+
+
+def test_wkv_bad_args(slim):
+    assert slim.lib.slim_wkv(None, None, 4, None, 0) == 1
+    a = np.eye(4)
+    out = np.empty((4, 4), np.float32)
+    assert slim.lib.slim_wkv(a.ctypes.data, a.ctypes.data, 4, out.ctypes.data, 5) == 2

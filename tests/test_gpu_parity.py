@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, element by element, at sizes the oracle finishes in
+seconds (several chunks, ragged tails, empty sequences), plus the invariants
+of the method.  Tolerance: max|o - o_ref| / max|o_ref| <= 1e-4 for fp32 caches
+and <= 2e-2 for bf16 caches."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from gpu_common import (TOL, bf16_bits, check_prefill_bf16, dev_wkv, gpu_decode, log, oracle_decode,
+                        to_dev)
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _check(name, o, ref, tol):
+    err = oracle.err_rel(o, ref)
+    log(f"[parity] {name}: err={err:.3e} tol={tol:.0e} max|ref|={np.abs(ref).max():.3e}")
+    assert np.isfinite(o).all()
+    assert err <= tol, f"{name}: err {err:.3e} > {tol}"
+    return err
+
+
+def _workload(cfg, fill=0.0):
+    wl = syn.make(cfg, fill=fill)
+    return wl
+
+
+def test_hand_example_fp32_path():
+    g = json.load(open(os.path.join(HERE, "golden", "hand_two_heads.json")))
+    cfg = syn.Config("hand", d=2, H=2, dh=1, B=1, T_max=2, len_lo=2, len_hi=2, cache="f32",
+                     wkv="f32", seed=0)
+    K = np.array([g["K"]], dtype=np.float32)
+    W = to_dev(np.array(g["W_KV"], dtype=np.float32))
+    o = gpu_decode(syn.Config(**{**cfg.__dict__}), np.array([g["q"]], dtype=np.float32), to_dev(K),
+                   np.array([2]), W)
+    # the fixture's scale is 1, the config's is 1/sqrt(1) = 1
+    _check("hand", o, np.array([g["o"]]), 1e-5)
+
+
+def test_c0_fp32():
+    cfg = syn.CONFIGS["c0"]
+    wl = _workload(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("c0", o, ref, TOL["f32"])
+
+
+def test_c0_fp32_ragged():
+    cfg = syn.shrink(syn.CONFIGS["c0"], B=5, T_max=45, len_lo=0, len_hi=45)
+    wl = _workload(cfg)
+    lens = np.array([0, 1, 45, 17, 60], dtype=np.int32)  # empty, single row, full, ragged, clamped
+    K = syn.k_cache(cfg, wl.w, np.minimum(lens, cfg.T_max))
+    o = gpu_decode(cfg, wl.q, to_dev(K), lens, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
+    assert np.all(o[0] == 0)
+    _check("c0-ragged", o, ref, TOL["f32"])
+
+
+def test_c1_bf16_full():
+    cfg = syn.CONFIGS["c1"]
+    wl = _workload(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("c1", o, ref, TOL["bf16"])
+
+
+def test_c2_shape_ragged_small():
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=6, T_max=1200, len_lo=1, len_hi=1200)
+    wl = _workload(cfg)
+    lens = wl.lengths.copy()
+    lens[1] = 0
+    lens[3] = 5000  # clamped to T_max
+    K = syn.k_cache(cfg, wl.w, np.minimum(lens, cfg.T_max))
+    o = gpu_decode(cfg, wl.q, to_dev(K), lens, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
+    assert np.all(o[1] == 0)
+    _check("c2-small", o, ref, TOL["bf16"])
+
+
+def test_c3_shape_16k():
+    cfg = syn.shrink(syn.CONFIGS["c3"], T_max=16384)
+    wl = _workload(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("c3-16k", o, ref, TOL["bf16"])
+
+
+def test_c4_prefill_then_decode_small():
+    """Whisper-shaped cross-attention: the K cache is written on the device
+    by slim_prefill from X and W_K; the oracle builds its own cache from the
+    same bf16 X and W_K in float64."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c4"], B=6)
+    wl = syn.make(cfg, with_cache=False)
+    Xb, Wb = syn.prefill_inputs(cfg, wl.w)
+    Kd = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
+    slim.prefill(to_dev(Xb), to_dev(Wb), Kd)
+    o = gpu_decode(cfg, wl.q, Kd, wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    K_ref = oracle.prefill(oracle.bf16_decode(Xb), oracle.bf16_decode(Wb), "bf16")
+    ref = oracle_decode(cfg, wl.q, K_ref, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("c4-small", o, ref, TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# prefill
+
+def test_prefill_bf16_matches_oracle():
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c4"], B=3, T_max=300)
+    w = syn.weights(cfg)
+    Xb, Wb = syn.prefill_inputs(cfg, w, n=300)
+    Kd = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
+    slim.prefill(to_dev(Xb), to_dev(Wb), Kd)
+    torch.cuda.synchronize()
+    check_prefill_bf16(bf16_bits(Kd), oracle.bf16_decode(Xb), oracle.bf16_decode(Wb), "c4-shape")
+
+
+def test_prefill_append_offsets_and_fp32():
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    rng = np.random.default_rng(5)
+    B, n, d, T = 3, 5, 72, 16
+    X = rng.standard_normal((B, n, d)).astype(np.float32)
+    W = rng.standard_normal((d, d)).astype(np.float32)
+    t0 = np.array([0, 7, 13], dtype=np.int32)  # the last one runs past T_max: rows >= T are skipped
+    Kd = torch.full((B, T, d), -7.0, dtype=torch.float32, device="cuda")
+    slim.prefill(to_dev(X), to_dev(W), Kd, t0=to_dev(t0))
+    torch.cuda.synchronize()
+    got = Kd.cpu().numpy()
+    ref = oracle.prefill(X, W, "f32")
+    for b in range(B):
+        for i in range(n):
+            t = t0[b] + i
+            if t < T:
+                assert np.abs(got[b, t] - ref[b, i]).max() <= 1e-5 * np.abs(ref).max()
+        untouched = [t for t in range(T) if not (t0[b] <= t < t0[b] + n)]
+        assert np.all(got[b, untouched] == -7.0)
+
+
+# ---------------------------------------------------------------------------
+# comparator (explicit K and V)
+
+@pytest.mark.parametrize("name,kw", [("c1", {}), ("c2", dict(B=5, T_max=900, len_lo=1, len_hi=900)),
+                                     ("c4", dict(B=4))])
+def test_comparator_matches_oracle(name, kw):
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS[name], **kw) if kw else syn.CONFIGS[name]
+    cfg = syn.Config(**{**cfg.__dict__, "prefill": False})
+    wl = syn.make(cfg)
+    V = syn.v_cache(cfg, wl.w, wl.lengths)
+    out = torch.empty((cfg.B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+    slim.mha_decode_kv(to_dev(wl.q), to_dev(wl.K), to_dev(V), to_dev(wl.lengths), out, cfg.H, cfg.dh,
+                       cfg.scale)
+    torch.cuda.synchronize()
+    ref = oracle.mha_decode(wl.q, oracle.cache_to_f64(wl.K), oracle.cache_to_f64(V), wl.lengths,
+                            cfg.H, cfg.dh, cfg.scale)
+    _check(f"kv-{name}", out.cpu().numpy(), ref, 1e-3)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+
+def test_rows_beyond_length_are_never_read():
+    """NaN garbage past len_b must not change a single output bit."""
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=4, T_max=700, len_lo=100, len_hi=650)
+    wl0 = syn.make(cfg, fill=0.0)
+    wln = syn.make(cfg, fill=float("nan"))
+    W = dev_wkv(cfg, wl0.w.W_K, wl0.w.W_V)
+    a = gpu_decode(cfg, wl0.q, to_dev(wl0.K), wl0.lengths, W)
+    b = gpu_decode(cfg, wln.q, to_dev(wln.K), wln.lengths, W)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("chunks", ["1", "3", "37", "200"])
+def test_chunk_count_invariance(monkeypatch, chunks):
+    """Any split of the token stream gives the same attention: every plan
+    meets the oracle bound, and plans differ from each other only by the
+    bf16 rounding of the softmax weights (taken against per-chunk maxima)."""
+    cfg = syn.shrink(syn.CONFIGS["c3"], T_max=3000)
+    wl = syn.make(cfg)
+    W = dev_wkv(cfg, wl.w.W_K, wl.w.W_V)
+    base = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, W)
+    import kv_cache_reduction_amd as slim
+    monkeypatch.setenv("SLIM_CHUNKS", chunks)
+    ws = slim.workspace(slim.decode_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, 1))
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, W, ws=ws)
+    ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    diff = oracle.err_rel(o, base)
+    log(f"[parity] chunks={chunks}: rel diff vs default plan {diff:.2e}")
+    _check(f"chunks={chunks}", o, ref, TOL["bf16"])
+    assert diff < 1e-2
+
+
+def test_phases_equal_full_call_and_deterministic():
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=3, T_max=700)
+    wl = syn.make(cfg)
+    W = dev_wkv(cfg, wl.w.W_K, wl.w.W_V)
+    Kd = to_dev(wl.K)
+    a = gpu_decode(cfg, wl.q, Kd, wl.lengths, W)
+    b = gpu_decode(cfg, wl.q, Kd, wl.lengths, W, phases=True)
+    c = gpu_decode(cfg, wl.q, Kd, wl.lengths, W)
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, c)
+
+
+def test_single_row_returns_value_row():
+    """len = 1: softmax is 1, so o_h = V[0, h] = (K[0] . W_KV)[h]."""
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=3, T_max=16, len_lo=1, len_hi=1)
+    wl = syn.make(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    V0 = oracle.explicit_values(wl.K[:, 0], wl.w.W_K, wl.w.W_V).reshape(cfg.B, cfg.H, cfg.dh)
+    _check("len1", o, V0, TOL["bf16"])
+
+
+def test_all_lengths_zero():
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=2, T_max=64)
+    wl = syn.make(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), np.zeros(2, np.int32), dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    assert np.all(o == 0)
+
+
+def test_workspace_too_small_is_rejected():
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=2, T_max=64)
+    wl = syn.make(cfg)
+    need = slim.decode_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, 1)
+    ws = slim.workspace(need - 256)
+    with pytest.raises(slim.SlimError) as e:
+        gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V), ws=ws[:need - 256])
+    assert e.value.status == 3

@@ -107,6 +107,15 @@ def test_explicit_values_matches_unrounded_mha_c0():
     assert _rel(V[0], X @ w.W_V) < 1e-5
 
 
+def test_explicit_values_cols_matches_full():
+    cfg = syn.shrink(syn.CONFIGS["c1"], T_max=96, B=2)
+    wl = syn.make(cfg)
+    cols = np.r_[64:128, 640:704]
+    full = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)[..., cols]
+    part = oracle.explicit_values_cols(wl.K, wl.w.W_K, wl.w.W_V, cols)
+    assert _rel(part, full) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # brute force
 
