@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s and K-cache GB/s (% HBM peak) at T=8K/128K, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
+ATTEND_SOURCES = ["kv_cache_reduction_amd/csrc/attend_bf16.hip", "kv_cache_reduction_amd/csrc/common.hpp",
+                  "kv_cache_reduction_amd/csrc/internal.hpp"]
 
 
 def log(*a):
@@ -144,6 +146,39 @@ def time_kv(wl, torch, slim, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def probe_copy_gbps(torch, slim, dst, src):
+    """Plain copy of a known size (read + write); its counter readings
+    calibrate FETCH_SIZE / WRITE_SIZE."""
+    for _ in range(2):
+        slim.probe_copy(dst, src)
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
+    n = 5
+    start.record()
+    for _ in range(n):
+        slim.probe_copy(dst, src)
+    stop.record()
+    torch.cuda.synchronize()
+    return 2 * src.numel() * src.element_size() / (start.elapsed_time(stop) / n * 1e-3) / 1e9
+
+
+def measured_traffic(kernel_sources):
+    """HBM bytes per attend launch from the committed counter summary, if the
+    counters were taken on the current kernel source; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attend_bf16_c3_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in kernel_sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
 def probe_read_gbps(torch, slim, src):
     sink = torch.empty(slim.probe_sink_floats(), dtype=torch.float32, device="cuda")
     for _ in range(3):
@@ -254,7 +289,8 @@ def main():
         "k_cache_gbps": k_gbps_step,
         "k_cache_hbm_frac": k_gbps_step / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": k_gbps_attend, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": k_gbps_attend / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": k_gbps_attend / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(ATTEND_SOURCES) if name == "c3" else None,
                      "kernel": "attend_bf16_kernel", "kernel_us": att_ms * 1e3,
                      "algorithmic_bytes": wl.k_bytes},
     }
@@ -268,6 +304,8 @@ def main():
         log(f"[bench] comparator: {ms_kv * 1e3:.1f} us/step, slim speedup {ms_kv / ms_step:.2f}x")
         res["probe_read_gbps"] = probe_read_gbps(torch, slim, wl.K[0])
         log(f"[bench] HBM read probe: {res['probe_read_gbps']:.0f} GB/s")
+        res["probe_copy_gbps"] = probe_copy_gbps(torch, slim, wl.K[1], wl.K[0])
+        log(f"[bench] HBM copy probe (read+write): {res['probe_copy_gbps']:.0f} GB/s")
         del wl
         torch.cuda.empty_cache()
         if name == "c3":

@@ -72,14 +72,24 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   if (nch > (1 << 20)) return false;
   p->nch = (int)nch;
   p->nslots = p->nch + B - 1;
-  p->npc = (d + kProjRows - 1) / kProjRows;
+  p->npc = (d + proj_rows(dh) - 1) / proj_rows(dh);
   size_t off = 0;
   p->off_U = off;
   off += align256((size_t)p->nslots * H * d * sizeof(float));
   p->off_ml = off;
   off += align256((size_t)p->nslots * 2 * H * sizeof(float));
+  p->off_u = off;
+  off += align256((size_t)B * H * d * sizeof(float));
   p->off_op = off;
   off += align256((size_t)p->npc * B * H * dh * sizeof(float));
+  // pair exchange: both workgroups of every chunk resident at once (one per CU)
+  p->pair = bf16_k && p->gc == 2 && (long long)p->nch * 2 <= ncu;
+  p->off_flags = off;
+  off += align256((size_t)p->nch * 2 * sizeof(unsigned long long));
+  p->off_x = off;
+  off += align256((size_t)p->nch * 2 * 4 * 256 * sizeof(float));
+  p->off_err = off;
+  off += 256;
   p->bytes = off;
   return true;
 }
@@ -178,8 +188,8 @@ static slim_status_t decode_common(int mode, const float* q, const void* K_cache
   slim_status_t st = decode_shape_ok(B, H, dh, T_max, k_dt);
   if (st != SLIM_OK) return st;
   if (w_dt != SLIM_F32 && w_dt != SLIM_BF16) return SLIM_ERR_UNSUPPORTED;
-  if (!aligned16(workspace) || !aligned16(K_cache) || ((uintptr_t)q & 3u) || ((uintptr_t)out & 3u) ||
-      ((uintptr_t)lengths & 3u) || ((uintptr_t)W_KV & (w_dt == SLIM_F32 ? 3u : 1u)))
+  if (!aligned16(workspace) || !aligned16(K_cache) || !aligned16(W_KV) || ((uintptr_t)q & 3u) ||
+      ((uintptr_t)out & 3u) || ((uintptr_t)lengths & 3u))
     return SLIM_ERR_INVALID;
   int ncu = 0;
   if (device_cus(&ncu) != 0) return SLIM_ERR_HIP;
@@ -197,6 +207,7 @@ static slim_status_t decode_common(int mode, const float* q, const void* K_cache
   a.dh = dh;
   a.d = H * dh;
   a.T_max = T_max;
+  a.nslots = plan.nslots;
   a.scale = scale;
   a.w_bf16 = w_dt == SLIM_BF16;
   a.ws = static_cast<char*>(workspace);

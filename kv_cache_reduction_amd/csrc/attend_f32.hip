@@ -20,7 +20,7 @@ struct AttendF32Params {
   const int32_t* lengths;
   float* U;
   float* ml;
-  int B, H, dh, d, T_max, nch, gcf;
+  int B, H, dh, d, T_max, nch, gcf, nslots;
   float qscale;
 };
 
@@ -84,10 +84,9 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
       __syncthreads();
     }
     if (col_ok) {
-      float* Us = p.U + (size_t)slot * p.H * p.d + col;
 #pragma unroll
       for (int h = 0; h < kF32MaxHeads; ++h)
-        if (h < p.H) Us[(size_t)h * p.d] = acc[h];
+        if (h < p.H) p.U[((size_t)h * p.nslots + slot) * p.d + col] = acc[h];
     }
     if (cb == 0 && tid < p.H) {
       p.ml[(size_t)slot * 2 * p.H + tid] = m;
@@ -110,6 +109,7 @@ hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStrea
   p.T_max = a.T_max;
   p.nch = pl.nch;
   p.gcf = pl.gc;
+  p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
   const size_t lds = (4 + 2 * kF32MaxHeads + (size_t)a.d + (size_t)a.B + 1) * 4;
   hipLaunchKernelGGL(attend_f32_kernel, dim3(pl.nch * pl.gc), dim3(256), lds, s, p);

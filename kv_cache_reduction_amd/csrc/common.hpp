@@ -59,6 +59,38 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 value split into two bf16 parts, hi = bf16(x), lo = bf16(x - hi);
+// hi + lo matches x to about 2^-16 relatively.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         acc, false);
+}
+
+// Sums of four per-lane values over each aligned row of 16 lanes, one result
+// per lane: lane r of the row ends with the total of value (2*(r&1) + ((r>>1)&1)).
+// Two exchange levels halve the values held per lane (xor 1, xor 2 quad
+// permutes), two row rotations (by 4 and by 8) finish the sums.
+__device__ __forceinline__ float row16_sum4(float v0, float v1, float v2, float v3, int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+  const float s0 = b0 ? v0 : v2, s1 = b0 ? v1 : v3;
+  const float k0 = b0 ? v2 : v0, k1 = b0 ? v3 : v1;
+  const float a0 = k0 + dpp_f<0xB1>(s0);  // partner lane ^ 1
+  const float a1 = k1 + dpp_f<0xB1>(s1);
+  const float sb = b1 ? a0 : a1, kb = b1 ? a1 : a0;
+  float x = kb + dpp_f<0x4E>(sb);         // partner lane ^ 2
+  x += dpp_f<0x124>(x);                   // row_ror:4
+  x += dpp_f<0x128>(x);                   // row_ror:8
+  return x;
+}
+
 // Raw buffer resource over [base, base + bytes): loads at byte offsets
 // outside the range return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

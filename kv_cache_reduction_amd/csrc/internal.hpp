@@ -18,10 +18,15 @@ struct DecodePlan {
   int nw;          // waves per workgroup (MFMA path)
   int nch;         // token chunks
   int nslots;      // partial slots
-  int npc;         // W_KV row chunks of the projection
-  size_t off_U;    // [nslots, H, d] float
+  int npc;         // W_KV row blocks of the projection (proj_rows(dh) rows each)
+  size_t off_U;    // [H, nslots, d] float: unnormalised softmax.K rows per chunk
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
-  size_t off_op;   // [npc, B, H, dh] float (per-row-chunk projection partials)
+  size_t off_u;    // [B, H, d] float: merged softmax.K rows
+  size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
+  bool pair;       // two column groups that exchange scores (grid fits the device at once)
+  size_t off_flags;  // [nch, 2] u64 step flags of the score exchange
+  size_t off_x;      // [nch, 2, 4, 32, 8] float exchanged scores
+  size_t off_err;    // int: exchange timeout seen
   size_t bytes;
 };
 
@@ -31,13 +36,14 @@ struct DecodeArgs {
   const int32_t* lengths;
   const void* W;
   float* out;
-  int B, H, dh, d, T_max;
+  int B, H, dh, d, T_max, nslots;
   float scale;
   bool w_bf16;
   char* ws;
 };
 
-constexpr int kProjRows = 128;     // W_KV rows per projection workgroup
+// W_KV rows per projection workgroup (keeps the per-thread slice <= 64 values)
+constexpr int proj_rows(int dh) { return dh > 128 ? 64 : 256; }
 constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
 constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)
 

@@ -144,44 +144,65 @@ __global__ void __launch_bounds__(512) mha_kv_split_kernel(KVParams p) {
 }
 
 // out[b, h, :] = sum_s 2^(m_s - m*) O_s[h, :] / sum_s 2^(m_s - m*) l_s
-__global__ void __launch_bounds__(64) mha_kv_combine_kernel(const int32_t* __restrict__ lengths,
-                                                            const float* __restrict__ O,
-                                                            const float* __restrict__ ml,
-                                                            float* __restrict__ out, int B, int H,
-                                                            int dh, int T_max, int nch) {
+// One 512-thread block per (b, h); thread t sums the float4 column group
+// t % (dh/4) over slot group t / (dh/4), then the groups are added in LDS.
+__global__ void __launch_bounds__(512) mha_kv_combine_kernel(const int32_t* __restrict__ lengths,
+                                                             const float* __restrict__ O,
+                                                             const float* __restrict__ ml,
+                                                             float* __restrict__ out, int B, int H,
+                                                             int dh, int T_max, int nch) {
   extern __shared__ int smem[];
-  int* tmp = smem;       // [1]
-  float* w = reinterpret_cast<float*>(smem + 4);  // [nch + 1]
-  int* pre = reinterpret_cast<int*>(w + nch + 1);  // [B + 1]
-  const int b = blockIdx.x / H, h = blockIdx.x % H, lane = threadIdx.x;
+  int* tmp = smem;                                  // [8]
+  float* red = reinterpret_cast<float*>(smem + 8);  // [2048]
+  float* w = red + 2048;                            // [nch + 1]
+  int* pre = reinterpret_cast<int*>(w + nch + 1);   // [B + 1]
+  const int b = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x;
   lengths_prefix(lengths, B, T_max, pre, tmp);
   const int s0 = pre[b], s1 = pre[b + 1];
   float* dst = out + ((size_t)b * H + h) * dh;
   if (s1 == s0) {
-    for (int j = lane; j < dh; j += 64) dst[j] = 0.f;
+    for (int j = tid; j < dh; j += blockDim.x) dst[j] = 0.f;
     return;
   }
   const int Ts = chunk_tokens(pre[B], nch);
   const int cf = s0 / Ts, cl = (s1 - 1) / Ts, ns = cl - cf + 1, slot0 = cf + b;
-  float m = kNegInf;
-  for (int i = lane; i < ns; i += 64) m = fmaxf(m, ml[(size_t)(slot0 + i) * 2 * H + h]);
+  __shared__ float inv_l;
+  if (tid < 64) {
+    float m = kNegInf;
+    for (int i = tid; i < ns; i += 64) m = fmaxf(m, ml[(size_t)(slot0 + i) * 2 * H + h]);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  float l = 0.f;
-  for (int i = lane; i < ns; i += 64) {
-    const float* e = ml + (size_t)(slot0 + i) * 2 * H;
-    const float wi = fast_exp2(e[h] - m);
-    w[i] = wi;
-    l += wi * e[H + h];
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float l = 0.f;
+    for (int i = tid; i < ns; i += 64) {
+      const float* e = ml + (size_t)(slot0 + i) * 2 * H;
+      const float wi = fast_exp2(e[h] - m);
+      w[i] = wi;
+      l += wi * e[H + h];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (tid == 0) inv_l = 1.f / l;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
   __syncthreads();
-  const float inv = 1.f / l;
-  for (int j = lane; j < dh; j += 64) {
-    float acc = 0.f;
-    for (int i = 0; i < ns; ++i) acc = fmaf(w[i], O[((size_t)(slot0 + i) * H + h) * dh + j], acc);
-    dst[j] = acc * inv;
+  const int c4 = dh / 4, ng = blockDim.x / c4;
+  const int j4 = tid % c4, g = tid / c4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = O + ((size_t)slot0 * H + h) * dh + 4 * j4;
+#pragma unroll 8
+  for (int i = g; i < ns; i += ng) {
+    const float4 v = *reinterpret_cast<const float4*>(src + (size_t)i * H * dh);
+    const float wi = w[i];
+    acc.x = fmaf(wi, v.x, acc.x);
+    acc.y = fmaf(wi, v.y, acc.y);
+    acc.z = fmaf(wi, v.z, acc.z);
+    acc.w = fmaf(wi, v.w, acc.w);
+  }
+  reinterpret_cast<float4*>(red)[g * c4 + j4] = acc;
+  __syncthreads();
+  for (int j = tid; j < dh; j += blockDim.x) {
+    float sum = 0.f;
+    for (int k = 0; k < ng; ++k) sum += red[k * dh + j];
+    dst[j] = sum * inv_l;
   }
 }
 
@@ -233,8 +254,8 @@ static hipError_t launch_kv_t(const KVPlan& pl, const float* q, const void* K, c
                      (16 + (size_t)B + 1) * 4, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mha_kv_combine_kernel, dim3(B * H), dim3(64),
-                     (4 + (size_t)pl.nch + 1 + (size_t)B + 1) * 4, s, lengths,
+  hipLaunchKernelGGL(mha_kv_combine_kernel, dim3(B * H), dim3(512),
+                     (8 + 2048 + (size_t)pl.nch + 1 + (size_t)B + 1) * 4, s, lengths,
                      (const float*)p.O, (const float*)p.ml, out, B, H, DH, T_max, pl.nch);
   return hipGetLastError();
 }
