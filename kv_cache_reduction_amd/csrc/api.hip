@@ -82,14 +82,6 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   off += align256((size_t)B * H * d * sizeof(float));
   p->off_op = off;
   off += align256((size_t)p->npc * B * H * dh * sizeof(float));
-  // pair exchange: both workgroups of every chunk resident at once (one per CU)
-  p->pair = bf16_k && p->gc == 2 && (long long)p->nch * 2 <= ncu;
-  p->off_flags = off;
-  off += align256((size_t)p->nch * 2 * sizeof(unsigned long long));
-  p->off_x = off;
-  off += align256((size_t)p->nch * 2 * 4 * 256 * sizeof(float));
-  p->off_err = off;
-  off += 256;
   p->bytes = off;
   return true;
 }

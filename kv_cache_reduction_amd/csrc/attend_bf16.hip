@@ -13,33 +13,37 @@
 //    each lane needs 4 tokens x 8 columns of the unit, exactly the register
 //    layout of the MFMA B operand (lane l: columns 8*(l%32)..+7 of tokens
 //    4*(l/32)..+3).  These bytes travel HBM -> LDS by buffer_load ... lds
-//    (16 bytes per lane, two 512-byte contiguous segments per instruction)
-//    into a ring private to the wave, `NST` steps ahead, so the registers
-//    only hold the step being computed.  The wave waits for its own ring
-//    slot with an explicit vmcnt; no other wave touches it.  Buffer
-//    resources bound each load to the piece's live rows, so the ragged tail
-//    reads as zeros without branches.
-//  * Scores come from the same registers: 8 fp32 FMAs per token per lane,
-//    then a DPP sum over the dh/8 lanes that share a head.  With gc == 2 each
-//    wave also loads the matching units of the other column group, for the
-//    scores only (every workgroup needs the softmax of all heads; the second
-//    read of a tile is meant to hit the XCD's L2).
-//  * Scores of all heads meet in a small double-buffered LDS array behind one
-//    barrier per step.  Every wave then runs the online softmax of all 32
-//    head rows (lane l: head l%32, tokens 4*(l/32)..+3, the MFMA A-operand
-//    layout), rounds the weights to bf16 and issues one 32x32 bf16 MFMA per 32
-//    output columns with B operands built by byte permutes (a 4x8 -> 8x4
+//    (16 bytes per lane, two 512-byte contiguous segments per instruction,
+//    non-temporal) into a ring private to the wave, `NST` steps ahead.  The
+//    wave waits for its own ring slot with an explicit vmcnt; no other wave
+//    touches it.  The buffer resource of each step starts at that step's
+//    first row and ends at the piece's last live row, so the ragged tail and
+//    the steps past the end read as zeros without branches.
+//  * Scores come from the same registers: split-q dot2 products (q as bf16
+//    high + low parts, so the products keep fp32 accuracy), then a DPP sum
+//    over the dh/8 lanes that share a head.  With gc == 2 each wave also
+//    loads the matching unit of the other column group, for the scores only
+//    (every workgroup needs the softmax of all heads; the second read of a
+//    tile mostly hits the XCD's L2).
+//  * Software pipeline, one barrier per step: in iteration i a wave reads
+//    the ring slot of step i+1, forms its heads' scores of step i+1 into the
+//    LDS score buffer S[(i+1)%2], and meanwhile runs the online softmax of
+//    step i from S[i%2] (written before the previous barrier) and the MFMAs
+//    of step i with the registers it read one iteration earlier.  The
+//    independent halves fill each other's latency.
+//  * Online softmax: lane l handles head l%32, tokens 4*(l/32)..+3 (the MFMA
+//    A-operand layout); weights are rounded to bf16 and one 32x32x16 bf16
+//    MFMA per 32 output columns takes the step's 8 tokens in the low half of
+//    its K dimension; B operands come from byte permutes (a 4x8 -> 8x4
 //    transpose of 16-bit values in registers).
 //  * Lazy rescaling: each head keeps a reference max m (log2 units) and the
 //    accumulator holds sum_t 2^(s_t - m) K[t]; m only moves (and the
 //    accumulator rows are rescaled) when a score exceeds it by more than 8,
 //    so weights stay below 2^8 and the rescale is rare.
 //  * Per piece (chunk x sequence) the workgroup writes its unnormalised
-//    accumulator U[slot, h, cols] and (column group 0) m and the normaliser
+//    accumulator U[h, slot, cols] and (column group 0) m and the normaliser
 //    l of every head.  q is pre-scaled by scale*log2(e); exponentials use
 //    v_exp_f32.
-#include <atomic>
-
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -55,19 +59,9 @@ struct AttendBf16Params {
   float qscale;
 };
 
-constexpr float kRescaleSlack = 8.f;  // log2 units
-
-__device__ __forceinline__ float dot8(const float4& qa, const float4& qb, const uint4& k) {
-  float s = qa.x * bf_lo(k.x);
-  s = fmaf(qa.y, bf_hi(k.x), s);
-  s = fmaf(qa.z, bf_lo(k.y), s);
-  s = fmaf(qa.w, bf_hi(k.y), s);
-  s = fmaf(qb.x, bf_lo(k.z), s);
-  s = fmaf(qb.y, bf_hi(k.z), s);
-  s = fmaf(qb.z, bf_lo(k.w), s);
-  s = fmaf(qb.w, bf_hi(k.w), s);
-  return s;
-}
+constexpr float kRescaleSlack = 8.f;         // log2 units
+constexpr uint32_t kOutOfRange = 0x80000000u;  // byte offset beyond any buffer resource used here
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;  // two bf16 1.0
 
 // q . k over 8 columns: q as packed bf16 hi/lo pairs (4 words each), k as
 // 8 bf16 in 4 words; two dot2 per column pair.
@@ -112,51 +106,11 @@ __device__ __forceinline__ void head_scores(const uint4& qh, const uint4& ql, co
   }
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-// acc[s] += P (32 heads x 8 tokens, A layout: lane l = head l%32, tokens
-// 4*(l/32)..+3 packed in w0, w1) times K (8 tokens x 256 columns held as
-// D[k] = 8 columns of token 4*(l/32)+k).  Column 8*(l%32) + s of the unit is
-// MFMA s's output column l%32.  On gfx950 the 32x32x16 instruction runs at
-// twice the rate of 32x32x8, so the 8 tokens fill half of its K=16 and the
-// other half is zero.
-#ifndef SLIM_MFMA_K8
-__device__ __forceinline__ void mfma_pk(f32x16 (&acc)[8], uint32_t w0, uint32_t w1, const uint4 (&D)[4]) {
-  const uint4 aw = make_uint4(w0, w1, 0u, 0u);
-  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, aw);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t sel = (s & 1) ? kSelHi : kSelLo;
-    const int wd = s >> 1;
-    const uint4 bw = make_uint4(perm(word(D[1], wd), word(D[0], wd), sel),
-                                perm(word(D[3], wd), word(D[2], wd), sel), 0u, 0u);
-    acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, bw), acc[s], 0, 0, 0);
-  }
-}
-#else
-__device__ __forceinline__ void mfma_pk(f32x16 (&acc)[8], uint32_t w0, uint32_t w1, const uint4 (&D)[4]) {
-  uint2 aw = make_uint2(w0, w1);
-  const s16x4 a = *reinterpret_cast<s16x4*>(&aw);
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const uint32_t sel = (s & 1) ? kSelHi : kSelLo;
-    const int wd = s >> 1;
-    uint2 bw;
-    bw.x = perm(word(D[1], wd), word(D[0], wd), sel);
-    bw.y = perm(word(D[3], wd), word(D[2], wd), sel);
-    const s16x4 bv = *reinterpret_cast<s16x4*>(&bw);
-    acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bv, acc[s], 0, 0, 0);
-  }
-}
-#endif
-
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Buffer descriptor (V#) for a raw byte range; loads beyond `bytes` return 0.
+// Buffer descriptor (V#) for a raw byte range; loads at offsets >= `bytes`
+// return 0.
 __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
@@ -170,18 +124,18 @@ __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// One 16-byte-per-lane load from a buffer straight into LDS: lane i's bytes
-// land at LDS byte address lds + 16*i.  Written as inline asm so that the
-// compiler does not drain the vector-memory counter at every workgroup
-// barrier (it treats LDS DMA as pending LDS stores); the kernel waits for
-// each ring slot itself with wait_vmcnt.
+// One 16-byte-per-lane non-temporal load from a buffer straight into LDS:
+// lane i's bytes land at LDS byte address lds + 16*i.  Written as inline asm
+// so that the compiler does not drain the vector-memory counter at every
+// workgroup barrier (it treats LDS DMA as pending LDS stores); the kernel
+// waits for each ring slot itself with wait_vmcnt.  No register is written.
 __device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc, uint32_t voff) {
   // `lds` and `rsrc` are wave-uniform; readfirstlane places them in SGPRs
   lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
       :
       : "s"(lds), "v"(voff), "s"(rsrc)
       : "memory");
@@ -194,17 +148,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
+// Both halves of the wave see the pair (x of lane l, x of lane l^32):
+// max / sum of the two equals the reduction over the two halves.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 template <int DH, int GC, int NST>
 __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
-  constexpr int LPH = DH / 8;          // lanes per head in a 32-lane half
-  constexpr int LPS = GC == 2 ? 8 : 4; // DMA instructions per step and wave
-  constexpr int SB = LPS * 1024;       // ring slot bytes per wave
+  static_assert(NST >= 2 && (NST & (NST - 1)) == 0, "ring slots: a power of two, at least 2");
+  constexpr int LPS = GC == 2 ? 8 : 4;  // DMA instructions per step and wave
+  constexpr int SB = LPS * 1024;        // ring slot bytes per wave (own unit, then other unit)
+  constexpr int WB = NST * SB;          // ring bytes per wave
   extern __shared__ __attribute__((aligned(16))) int smem[];
   const int nw = blockDim.x >> 6;
-  char* ring = reinterpret_cast<char*>(smem);                        // [nw][NST][SB]
-  float* S = reinterpret_cast<float*>(ring + (size_t)nw * NST * SB);  // [2][32][8]
-  int* tmp = reinterpret_cast<int*>(S + 512);                         // [16]
-  int* pre = tmp + 16;                                                // [B+1]
+  char* ring = reinterpret_cast<char*>(smem);                     // [nw][NST][SB]
+  float* S = reinterpret_cast<float*>(ring + (size_t)nw * WB);     // [2][32][8]
+  int* tmp = reinterpret_cast<int*>(S + 512);                      // [16]
+  int* pre = tmp + 16;                                             // [B+1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -225,8 +188,12 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
     }
   }
 
-  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);
-  const int total = pre[p.B];
+  // score rows of heads >= H are never written and stay -inf (weight 0)
+  for (int i = tid; i < 512; i += blockDim.x) S[i] = kNegInf;
+  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);  // (ends with a barrier)
+  // values read from LDS are uniform here; readfirstlane keeps the step
+  // arithmetic on the scalar unit
+  const int total = __builtin_amdgcn_readfirstlane(pre[p.B]);
   if (total == 0) return;
   const int Ts = chunk_tokens(total, p.nch);
   const int cbeg = c * Ts;
@@ -234,19 +201,34 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
   const int cend = min(total, cbeg + Ts);
 
   const int d = p.d;
-  const int ub = wave * kMfmaUnitCols + 8 * l32;
-  const int ocol = cg * p.dc + ub;
-  const bool ook = ocol < min(d, (cg + 1) * p.dc);
-  const int xcol = (1 - cg) * p.dc + ub;
+  const int ubase = cg * p.dc + wave * kMfmaUnitCols;  // first column of this wave's unit
+  const int clim = min(d, (cg + 1) * p.dc);            // end of this column group
+  const int ocol = ubase + 8 * l32;
+  const bool ook = ocol < clim;
+  const int xcol = (1 - cg) * p.dc + wave * kMfmaUnitCols + 8 * l32;
   const bool xok = GC == 2 && xcol < min(d, (2 - cg) * p.dc);
-  const bool score_lane = (l32 % LPH) == 0;
-  const bool head_ok = l32 < p.H;
-  const uint32_t ring_w = (uint32_t)reinterpret_cast<uintptr_t>(ring + (size_t)wave * NST * SB);
-  const uint4* ring_rd = reinterpret_cast<const uint4*>(ring + (size_t)wave * NST * SB) + lane;
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const uint32_t step_bytes = row_bytes * kStepTokens;
+  // byte offset of this lane's first row within a step (row k adds k rows);
+  // columns outside the column range read as zero
+  const uint32_t vo = ook ? (uint32_t)(half * 4) * row_bytes + (uint32_t)ocol * 2u : kOutOfRange;
+  const uint32_t vx = xok ? (uint32_t)(half * 4) * row_bytes + (uint32_t)xcol * 2u : kOutOfRange;
+  // LDS: a slot holds the step's 8 rows x 256 columns of the own unit (and
+  // then of the other unit), row t at (t%4)*1024 + (t/4)*512, column c at +2c
+  // (the order the DMA writes them)
+  char* wring = ring + (size_t)wave * WB;
+  const uint32_t wring_s = (uint32_t)reinterpret_cast<uintptr_t>(wring);  // LDS byte address
+  const uint4* rd16 = reinterpret_cast<const uint4*>(wring) + lane;
+  // transpose read (ds_read_b64_tr_b16) feeding MFMA s its B operand: lane
+  // L points at 4 columns 32s + 16*((L/16)%2) + 4*(L%4).. of row
+  // 4*(L/32) + (L%16)/4; the 16-lane transpose then leaves output lane l with
+  // column 32s + l%32 of rows 4*(l/32)..+3
+  const int tr_off = ((lane & 15) >> 2) * 1024 + (lane >> 5) * 512 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
 
   int gstep = 0;  // step counter across pieces: parity selects the S buffer
-  for (int b = seq_of(pre, p.B, cbeg); b < p.B && pre[b] < cend; ++b) {
-    const int s0 = pre[b], s1 = pre[b + 1];
+  for (int b = __builtin_amdgcn_readfirstlane(seq_of(pre, p.B, cbeg)); b < p.B; ++b) {
+    const int s0 = __builtin_amdgcn_readfirstlane(pre[b]), s1 = __builtin_amdgcn_readfirstlane(pre[b + 1]);
+    if (s0 >= cend) break;
     if (s1 == s0) continue;
     const int tb = max(cbeg, s0) - s0;
     const int n = min(cend, s1) - s0 - tb;
@@ -259,69 +241,93 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
       split_q8(qb + (xok ? xcol : 0), p.qscale, qxh, qxl);
     }
 
-    const uint32_t nbytes = (uint32_t)n * (uint32_t)d * 2u;
-    const i32x4 rs = buffer_desc(p.K + ((size_t)b * p.T_max + tb) * d, nbytes);
-    // byte offset of this lane's row 4*half of step 0; columns outside the
-    // column range point past the resource and read as zero
-    const uint32_t row_bytes = (uint32_t)d * 2u;
-    const uint32_t step_bytes = row_bytes * kStepTokens;
-    const uint32_t ooff = ook ? ((uint32_t)(half * 4) * d + ocol) * 2u : nbytes;
-    const uint32_t xoff = xok ? ((uint32_t)(half * 4) * d + xcol) * 2u : nbytes;
-    const uint32_t ostep = ook ? step_bytes : 0u, xstep = xok ? step_bytes : 0u;
-
-    auto issue = [&](int step, int stage) {
-      const uint32_t dst = ring_w + stage * SB;
+    const uint16_t* kbase = p.K + ((size_t)b * p.T_max + tb) * d;
+    const uint32_t nbytes = (uint32_t)n * row_bytes;  // < 2^31 (launch plan)
+    // ring slot `sl` <- step `step`; the buffer resource runs from the step's
+    // first row to the piece's end (rows past the piece, and whole steps
+    // past it, read as zeros)
+    auto issue = [&](int step, int sl) {
+      const uint32_t done = (uint32_t)step * step_bytes;
+      const uint32_t left = nbytes > done ? nbytes - done : 0u;
+      const i32x4 rs = buffer_desc(reinterpret_cast<const char*>(kbase) + (left ? done : 0u), left);
+      const uint32_t dst = wring_s + sl * SB;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dma16(dst + k * 1024, rs, ooff + step * ostep + k * row_bytes);
+      for (int k = 0; k < 4; ++k) dma16(dst + k * 1024, rs, vo + k * row_bytes);
       if (GC == 2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dma16(dst + 4096 + k * 1024, rs, xoff + step * xstep + k * row_bytes);
+        for (int k = 0; k < 4; ++k) dma16(dst + 4096 + k * 1024, rs, vx + k * row_bytes);
       }
     };
+    // scores of the step in slot `sl` (own and other unit) -> Sb
+    auto scores = [&](int sl, float* Sb) {
+      uint4 ko[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ko[k] = rd16[(sl * SB + k * 1024) / 16];
+      head_scores<DH>(qoh, qol, ko, ook, ocol, lane, half, Sb);
+      if (GC == 2) {
+        uint4 kx[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kx[k] = rd16[(sl * SB + 4096 + k * 1024) / 16];
+        head_scores<DH>(qxh, qxl, kx, xok, xcol, lane, half, Sb);
+      }
+    };
+    // MFMA B operands of the step in slot `sl`
+    auto b_operands = [&](int sl, s16x4 (&bop)[8]) {
+      const lds_s16x4* a0 = (const lds_s16x4*)(size_t)(wring_s + (uint32_t)(sl * SB + tr_off));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) bop[s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(a0 + 8 * s));
+    };
 
-    float m_ref = kNegInf, l_run = 0.f;  // head l32 (both halves hold copies)
+    float m_ref = kNegInf, l_half = 0.f;  // head l32; l_half sums this half's tokens
     f32x16 acc[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[s] = f32x16{0};
 
     const int nsteps = (n + kStepTokens - 1) / kStepTokens;
+    // prologue: steps 0..NST-1 in flight; scores and B operands of step 0;
+    // step NST refills slot 0
+    s16x4 bcur[8];
 #pragma unroll
-    for (int s = 0; s < NST; ++s) issue(s, s);  // steps past the end read zeros
+    for (int s = 0; s < NST; ++s) issue(s, s);
+    wait_vmcnt<(NST - 1) * LPS>();
+    scores(0, S + (gstep & 1) * 256);
+    b_operands(0, bcur);
+    wait_lgkmcnt0();
+    issue(NST, 0);
+    __syncthreads();
 
     for (int st = 0; st < nsteps; ++st) {
-      const int stage = st % NST;
+      float* Sc = S + ((gstep + st) & 1) * 256;
+      float* Sn = S + ((gstep + st + 1) & 1) * 256;
+      const int sl = (st + 1) & (NST - 1);
+      // slot sl holds step st+1 (past the end: zeros); steps st+2.. may
+      // still be in flight.  Scores and B operands of step st+1, then the
+      // slot goes back in flight with step st+1+NST.  S[st+1] was last read
+      // before the previous barrier.
       wait_vmcnt<(NST - 1) * LPS>();
-      uint4 ko[4], kx[4];
+      scores(sl, Sn);
+      s16x4 bnext[8];
+      b_operands(sl, bnext);
+
+      // online softmax of step st: head l32, tokens 4*half..+3
+      const float4 sv = *reinterpret_cast<const float4*>(Sc + l32 * 8 + half * 4);
+      float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+      if ((st + 1) * kStepTokens > n) {  // ragged last step
+        const int t0 = st * kStepTokens + half * 4;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ko[k] = ring_rd[(stage * SB + k * 1024) / 16];
-      if (GC == 2) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) kx[k] = ring_rd[(stage * SB + 4096 + k * 1024) / 16];
+        for (int k = 0; k < 4; ++k) sc[k] = t0 + k < n ? sc[k] : kNegInf;
       }
       wait_lgkmcnt0();
-      issue(st + NST, stage);
+      issue(st + 1 + NST, sl);
 
-      float* Sb = S + (gstep & 1) * 256;
-      ++gstep;
-      // 1. scores of the heads whose columns this lane holds
-      head_scores<DH>(qoh, qol, ko, ook, ocol, lane, half, Sb);
-      if (GC == 2) head_scores<DH>(qxh, qxl, kx, xok, xcol, lane, half, Sb);
-      __syncthreads();
-
-      // 2. online softmax, head l32, tokens 4*half..+3 of the step
-      const float4 sv = *reinterpret_cast<const float4*>(Sb + l32 * 8 + half * 4);
-      float sc[4] = {sv.x, sv.y, sv.z, sv.w};
-      const int t0 = st * kStepTokens + half * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (!head_ok || t0 + k >= n) sc[k] = kNegInf;
-      float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      float ma, mb;
+      halves(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), ma, mb);
+      const float mt = fmaxf(ma, mb);
       const bool grow = mt > m_ref + kRescaleSlack;
       if (__any(grow)) {  // rare: move the reference max and rescale
         const float m_new = grow ? mt : m_ref;
         const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
-        l_run *= alpha;
+        l_half *= alpha;
         m_ref = m_new;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -330,297 +336,47 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
           for (int s = 0; s < 8; ++s) acc[s][e] *= ar;
         }
       }
-      float pk[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pk[k] = (m_ref == kNegInf) ? 0.f : fast_exp2(sc[k] - m_ref);
-      const uint32_t w0 = pack_bf16x2(pk[0], pk[1]);
-      const uint32_t w1 = pack_bf16x2(pk[2], pk[3]);
-      float ps = (bf_lo(w0) + bf_hi(w0)) + (bf_lo(w1) + bf_hi(w1));
-      ps += __shfl_xor(ps, 32, 64);
-      l_run += ps;
+      // m_ref is finite once any score of the head was finite; masked
+      // scores (-inf) give weight 0 either way
+      const float mu = fmaxf(m_ref, -__FLT_MAX__);
+      const bf16x2_t p01 = {(__bf16)fast_exp2(sc[0] - mu), (__bf16)fast_exp2(sc[1] - mu)};
+      const bf16x2_t p23 = {(__bf16)fast_exp2(sc[2] - mu), (__bf16)fast_exp2(sc[3] - mu)};
+      const uint32_t w0 = __builtin_bit_cast(uint32_t, p01);
+      const uint32_t w1 = __builtin_bit_cast(uint32_t, p23);
+      l_half = dot2_bf16(w1, kOnesBf16x2, dot2_bf16(w0, kOnesBf16x2, l_half));
 
-      // 3. softmax weights (A: heads x tokens) times K (B: tokens x columns)
-      mfma_pk(acc, w0, w1, ko);
+      // softmax weights (A: 32 heads x 8 tokens) times K (B: 8 tokens x 32
+      // columns), MFMA s covering columns 32s..32s+31 of the unit
+      {
+        uint2 aw = make_uint2(w0, w1);
+        const s16x4 a = __builtin_bit_cast(s16x4, aw);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bcur[s], acc[s], 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) bcur[s] = bnext[s];
+      __syncthreads();
     }
+    gstep += nsteps + 1;
     wait_vmcnt<0>();  // the loads issued past the end have landed before the ring is reused
 
-    // 4. partial results of this piece
+    // partial results of this piece: MFMA s, lane l, element e holds head
+    // 8*(e/4) + 4*(l/32) + e%4 at unit column 32s + l%32
+    float la, lb;
+    halves(l_half, la, lb);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = 8 * (e >> 2) + 4 * half + (e & 3);
-      if (ook && row < p.H) {
-        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ocol;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][e], acc[5][e], acc[6][e], acc[7][e]);
+      if (row < p.H) {
+        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ubase + l32;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (ubase + 32 * s + l32 < clim) dst[32 * s] = acc[s][e];
       }
     }
     if (cg == 0 && wave == 0 && lane < p.H) {
       p.ml[(size_t)slot * 2 * p.H + lane] = m_ref;
-      p.ml[(size_t)slot * 2 * p.H + p.H + lane] = l_run;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Pair kernel (two column groups): each workgroup of a pair forms the scores
-// of its own heads only (the heads whose columns lie in its column group)
-// from its own half of K, and the pair exchange those scores through memory
-// once per step; both then run the softmax of all heads and multiply by their
-// own columns.  K is read once, and the score work is not duplicated.
-//
-// Step pipeline (step i, global step counter g):
-//   [A] scores of step i+1 (registers D_next) -> S[(g+1)%3] own heads; the
-//       loading waves wait for ring slot of step i+2.
-//   barrier
-//   [B] wave 0 publishes its heads' scores of step i+1 (write-through stores,
-//       its own vmcnt(0), then the step flag) and waits for the partner's
-//       scores of step i, which it copies into S[g%3]; the loading waves refill
-//       the ring slot of step i+1 with step i+1+NST.
-//   barrier
-//   [C] online softmax of step i over all heads, MFMA with D_cur, then
-//       D_cur <- D_next, D_next <- ring slot of step i+2.
-// Wave 0 issues no ring loads (wave nw/2 loads its unit), so its vmcnt covers
-// only its own exchange stores.  Flags carry a per-launch epoch in the high
-// 32 bits; waits are bounded and a timeout is recorded in `err` and turns the
-// outputs into NaN instead of hanging.
-constexpr int kExchSlots = 4;
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-struct PairParams {
-  AttendBf16Params a;
-  unsigned long long* flags;  // [nch][2]
-  float* xbuf;                // [nch][2][kExchSlots][32][8]
-  int* err;
-  uint32_t epoch;
-};
-
-__device__ __forceinline__ void store_wt(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_wt(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int DH, int NST>
-__global__ void __launch_bounds__(512) attend_pair_kernel(PairParams pp) {
-  static_assert(NST >= 3, "pipeline needs three ring slots");
-  constexpr int LPH = DH / 8;
-  constexpr int SB = 4 * 1024;  // one 256-column unit x 8 tokens per wave and slot
-  const AttendBf16Params& p = pp.a;
-  extern __shared__ __attribute__((aligned(16))) int smem[];
-  const int nw = blockDim.x >> 6;
-  char* ring = reinterpret_cast<char*>(smem);                         // [nw][NST][SB]
-  float* S = reinterpret_cast<float*>(ring + (size_t)nw * NST * SB);  // [3][32][8]
-  int* tmp = reinterpret_cast<int*>(S + 3 * 256);                // [16]
-  int* pre = tmp + 16;                                           // [B+1]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-
-  int c, cg;
-  {
-    const int bid = blockIdx.x;
-    if ((p.nch & 7) == 0) {
-      const int xcd = bid & 7, k = bid >> 3;
-      cg = k & 1;
-      c = ((k >> 1) << 3) + xcd;
-    } else {
-      c = bid >> 1;
-      cg = bid & 1;
-    }
-  }
-  unsigned long long* my_flag = pp.flags + (size_t)c * 2 + cg;
-  const unsigned long long* pa_flag = pp.flags + (size_t)c * 2 + (1 - cg);
-  float* my_x = pp.xbuf + ((size_t)c * 2 + cg) * kExchSlots * 256;
-  const float* pa_x = pp.xbuf + ((size_t)c * 2 + (1 - cg)) * kExchSlots * 256;
-  const unsigned long long ep = (unsigned long long)pp.epoch << 32;
-
-  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);
-  const int total = pre[p.B];
-  if (total == 0) return;
-  const int Ts = chunk_tokens(total, p.nch);
-  const int cbeg = c * Ts;
-  if (cbeg >= total) return;
-  const int cend = min(total, cbeg + Ts);
-
-  const int d = p.d;
-  const int own_lo = cg * p.dc, own_hi = min(d, (cg + 1) * p.dc);
-  const int ocol = own_lo + wave * kMfmaUnitCols + 8 * l32;
-  const bool ook = ocol < own_hi;
-  // heads whose columns lie in this column group, and the partner's
-  const int h_lo = own_lo / DH, h_hi = own_hi / DH;
-  const bool score_lane = (l32 % LPH) == 0;
-  const bool head_ok = l32 < p.H;
-  // ring loads: wave w loads its own unit; wave nw/2 also loads wave 0's
-  const bool loader = wave != 0;
-  const bool extra = wave == (nw >> 1);
-  const int ocol0 = own_lo + 8 * l32;  // wave 0's columns (for wave 4)
-  const bool ook0 = ocol0 < own_hi;
-  const uint32_t ring_w = (uint32_t)reinterpret_cast<uintptr_t>(ring + (size_t)wave * NST * SB);
-  const uint32_t ring_0 = (uint32_t)reinterpret_cast<uintptr_t>(ring);
-  const uint4* ring_rd = reinterpret_cast<const uint4*>(ring + (size_t)wave * NST * SB) + lane;
-
-  unsigned long long gstep = 0;  // steps published so far across pieces
-  bool failed = false;
-  for (int b = seq_of(pre, p.B, cbeg); b < p.B && pre[b] < cend; ++b) {
-    const int s0 = pre[b], s1 = pre[b + 1];
-    if (s1 == s0) continue;
-    const int tb = max(cbeg, s0) - s0;
-    const int n = min(cend, s1) - s0 - tb;
-    const int slot = c + b;
-
-    uint4 qh, ql;
-    split_q8(p.q + (size_t)b * d + (ook ? ocol : 0), p.qscale, qh, ql);
-    const uint32_t nbytes = (uint32_t)n * (uint32_t)d * 2u;
-    const i32x4 rs = buffer_desc(p.K + ((size_t)b * p.T_max + tb) * d, nbytes);
-    const uint32_t row_bytes = (uint32_t)d * 2u;
-    const uint32_t step_bytes = row_bytes * kStepTokens;
-    // lanes whose columns lie outside the group start past the resource, so
-    // every later row of theirs stays out of range too (offsets stay < 2^32)
-    const uint32_t ooff = ook ? ((uint32_t)(half * 4) * d + ocol) * 2u : nbytes;
-    const uint32_t ooff0 = ook0 ? ((uint32_t)(half * 4) * d + ocol0) * 2u : nbytes;
-    auto issue = [&](int step) {
-      const int stage = step % NST;
-      const uint32_t sb = (uint32_t)step * step_bytes;
-      if (loader) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dma16(ring_w + stage * SB + k * 1024, rs, ooff + sb + k * row_bytes);
-      }
-      if (extra) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) dma16(ring_0 + stage * SB + k * 1024, rs, ooff0 + sb + k * row_bytes);
-      }
-    };
-    // wait until the ring slot of step `ahead` steps before the newest issued one has landed
-    auto wait_ring = [&]() {
-      if (extra) wait_vmcnt<(NST - 2) * 8>();
-      else if (loader) wait_vmcnt<(NST - 2) * 4>();
-    };
-    auto read_ring = [&](int step, uint4 (&D)[4]) {
-      const int stage = step % NST;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) D[k] = ring_rd[(stage * SB + k * 1024) / 16];
-    };
-    auto scores = [&](int step, const uint4 (&D)[4], float* Sb) {
-      head_scores<DH>(qh, ql, D, ook, ocol, lane, half, Sb);
-    };
-    // wave 0: publish own heads' scores of a step, then fetch the partner's
-    auto publish = [&](const float* Sb, unsigned long long g) {
-      float* dst = my_x + (g % kExchSlots) * 256;
-      for (int i = lane; i < (h_hi - h_lo) * 8; i += 64) store_wt(dst + h_lo * 8 + i, Sb[h_lo * 8 + i]);
-      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-      if (lane == 0) __hip_atomic_store(my_flag, ep | (g + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto fetch = [&](float* Sb, unsigned long long g) {
-      bool ok = true;
-      if (lane == 0) {
-        uint32_t spins = 0;
-        for (;;) {
-          const unsigned long long f = __hip_atomic_load(const_cast<unsigned long long*>(pa_flag),
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((f >> 32) == pp.epoch && (f & 0xffffffffull) >= g + 1) break;
-          if (++spins >= kSpinLimit) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      ok = __shfl(ok ? 1 : 0, 0, 64) != 0;
-      if (!ok) failed = true;
-      const float* src = pa_x + (g % kExchSlots) * 256;
-      for (int i = lane; i < 256; i += 64) {
-        const int hh = i >> 3;
-        if (hh < h_lo || hh >= h_hi) Sb[i] = ok ? load_wt(src + i) : __builtin_nanf("");
-      }
-    };
-
-    float m_ref = kNegInf, l_run = 0.f;
-    f32x16 acc[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc[s] = f32x16{0};
-    const int nsteps = (n + kStepTokens - 1) / kStepTokens;
-
-    // prologue: ring slots for steps 0..NST-1, scores of step 0, publish it
-#pragma unroll
-    for (int s = 0; s < NST; ++s) issue(s);
-    wait_ring();
-    __syncthreads();
-    uint4 Dc[4], Dn[4];
-    read_ring(0, Dc);
-    read_ring(1, Dn);
-    scores(0, Dc, S + (gstep % 3) * 256);
-    __syncthreads();
-    issue(NST);  // refill the slot of step 0
-    if (wave == 0) publish(S + (gstep % 3) * 256, gstep);
-
-    for (int st = 0; st < nsteps; ++st) {
-      const unsigned long long g = gstep + st;
-      float* Sc = S + (g % 3) * 256;
-      float* Sn = S + ((g + 1) % 3) * 256;
-      // [A]
-      if (st + 1 < nsteps) scores(st + 1, Dn, Sn);
-      wait_ring();
-      __syncthreads();
-      // [B]
-      if (wave == 0) {
-        if (st + 1 < nsteps) publish(Sn, g + 1);
-        fetch(Sc, g);
-      }
-      issue(st + 1 + NST);
-      __syncthreads();
-      // [C] online softmax over all heads, tokens 4*half..+3 of step st
-      const float4 sv = *reinterpret_cast<const float4*>(Sc + l32 * 8 + half * 4);
-      float sc[4] = {sv.x, sv.y, sv.z, sv.w};
-      const int t0 = st * kStepTokens + half * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (!head_ok || t0 + k >= n) sc[k] = kNegInf;
-      float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const bool grow = mt > m_ref + kRescaleSlack;
-      if (__any(grow)) {
-        const float m_new = grow ? mt : m_ref;
-        const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
-        l_run *= alpha;
-        m_ref = m_new;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float ar = __shfl(alpha, 8 * (e >> 2) + 4 * half + (e & 3), 64);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) acc[s][e] *= ar;
-        }
-      }
-      float pk[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pk[k] = (m_ref == kNegInf) ? 0.f : fast_exp2(sc[k] - m_ref);
-      const uint32_t w0 = pack_bf16x2(pk[0], pk[1]);
-      const uint32_t w1 = pack_bf16x2(pk[2], pk[3]);
-      float ps = (bf_lo(w0) + bf_hi(w0)) + (bf_lo(w1) + bf_hi(w1));
-      ps += __shfl_xor(ps, 32, 64);
-      l_run += ps;
-      mfma_pk(acc, w0, w1, Dc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Dc[k] = Dn[k];
-      if (st + 2 < nsteps) read_ring(st + 2, Dn);
-    }
-    gstep += nsteps;
-    if (loader) wait_vmcnt<0>();  // loads issued past the end have landed before the ring is reused
-    __syncthreads();
-
-    if (failed && lane == 0) atomicExch(pp.err, 1);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * half + (e & 3);
-      if (ook && row < p.H) {
-        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ocol;
-        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][e], acc[5][e], acc[6][e], acc[7][e]);
-      }
-    }
-    if (cg == 0 && wave == 0 && lane < p.H) {
-      p.ml[(size_t)slot * 2 * p.H + lane] = failed ? __builtin_nanf("") : m_ref;
-      p.ml[(size_t)slot * 2 * p.H + p.H + lane] = l_run;
+      p.ml[(size_t)slot * 2 * p.H + p.H + lane] = la + lb;
     }
   }
 }
@@ -628,7 +384,7 @@ __global__ void __launch_bounds__(512) attend_pair_kernel(PairParams pp) {
 template <int DH, int GC>
 static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = GC == 2 ? 2 : 4;
-  constexpr int SB = (GC == 2 ? 8 : 4) * 1024;
+  constexpr int WB = NST * (GC == 2 ? 8 : 4) * 1024;
   AttendBf16Params p;
   p.q = a.q;
   p.K = static_cast<const uint16_t*>(a.K);
@@ -643,7 +399,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   p.dc = pl.dc;
   p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
-  const size_t lds = (size_t)pl.nw * NST * SB + (512 + 16 + (size_t)a.B + 1) * sizeof(int);
+  const size_t lds = (size_t)pl.nw * WB + (512 + 16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_bf16_kernel<DH, GC, NST>;
   static int lds_allowed = 0;  // largest dynamic LDS size already granted to this kernel
   if ((int)lds > lds_allowed) {
@@ -656,62 +412,6 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   return hipGetLastError();
 }
 
-// Per-launch epoch of the pair exchange flags: distinct for every launch of
-// the process, starting from a value unlikely to match stale workspace bytes.
-static uint32_t next_epoch() {
-  static std::atomic<uint32_t> ctr{0x5a17c0deu ^ (uint32_t)(reinterpret_cast<uintptr_t>(&ctr) >> 4)};
-  uint32_t e = ctr.fetch_add(1) + 1;
-  return e == 0 ? 1 : e;
-}
-
-// Returns hipSuccess when the pair kernel was launched, hipErrorNotSupported
-// when the plan or device does not allow it (the caller then uses the
-// two-column-group kernel that recomputes all scores in each workgroup).
-template <int DH>
-static hipError_t launch_pair(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
-  constexpr int NST = 4;
-  constexpr int SB = 4 * 1024;
-  if (pl.gc != 2 || pl.nw < 2 || !pl.pair || env_int("SLIM_PAIR", 0) == 0) return hipErrorNotSupported;
-  PairParams pp;
-  AttendBf16Params& p = pp.a;
-  p.q = a.q;
-  p.K = static_cast<const uint16_t*>(a.K);
-  p.lengths = a.lengths;
-  p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
-  p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
-  p.B = a.B;
-  p.H = a.H;
-  p.d = a.d;
-  p.T_max = a.T_max;
-  p.nch = pl.nch;
-  p.dc = pl.dc;
-  p.nslots = pl.nslots;
-  p.qscale = a.scale * kLog2e;
-  pp.flags = reinterpret_cast<unsigned long long*>(a.ws + pl.off_flags);
-  pp.xbuf = reinterpret_cast<float*>(a.ws + pl.off_x);
-  pp.err = reinterpret_cast<int*>(a.ws + pl.off_err);
-  pp.epoch = next_epoch();
-  const size_t lds = (size_t)pl.nw * NST * SB + (3 * 256 + 16 + (size_t)a.B + 1) * sizeof(int);
-  auto kern = attend_pair_kernel<DH, NST>;
-  static int lds_allowed = 0;
-  if ((int)lds > lds_allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return hipErrorNotSupported;
-    lds_allowed = (int)lds;
-  }
-  // the two workgroups of a pair wait on each other: they must be resident
-  // together, which a cooperative launch guarantees (or refuses)
-  void* args[] = {&pp};
-  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(pl.nch * 2),
-                                            dim3(pl.nw * 64), args, (unsigned)lds, s);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();  // clear the refusal
-    return hipErrorNotSupported;
-  }
-  return hipSuccess;
-}
-
 hipError_t launch_attend_bf16(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   if (pl.gc == 1) {
     switch (a.dh) {
@@ -720,13 +420,6 @@ hipError_t launch_attend_bf16(const DecodePlan& pl, const DecodeArgs& a, hipStre
       case 128: return launch_t<128, 1>(pl, a, s);
     }
   } else {
-    hipError_t e = hipErrorNotSupported;
-    switch (a.dh) {
-      case 32: e = launch_pair<32>(pl, a, s); break;
-      case 64: e = launch_pair<64>(pl, a, s); break;
-      case 128: e = launch_pair<128>(pl, a, s); break;
-    }
-    if (e != hipErrorNotSupported) return e;
     switch (a.dh) {
       case 32: return launch_t<32, 2>(pl, a, s);
       case 64: return launch_t<64, 2>(pl, a, s);

@@ -23,10 +23,6 @@ struct DecodePlan {
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
   size_t off_u;    // [B, H, d] float: merged softmax.K rows
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
-  bool pair;       // two column groups that exchange scores (grid fits the device at once)
-  size_t off_flags;  // [nch, 2] u64 step flags of the score exchange
-  size_t off_x;      // [nch, 2, 4, 32, 8] float exchanged scores
-  size_t off_err;    // int: exchange timeout seen
   size_t bytes;
 };
 
