@@ -82,6 +82,9 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   off += align256((size_t)B * H * d * sizeof(float));
   p->off_op = off;
   off += align256((size_t)p->npc * B * H * dh * sizeof(float));
+  p->xchg = bf16_k && p->gc == 2 && dh == 128 && 2 * p->dc == d && p->nw == 8;
+  p->off_mbox = off;
+  off += p->xchg ? align256((size_t)p->nch * 2 * 8 * 8 * 16 * sizeof(unsigned long long)) : 0;
   p->bytes = off;
   return true;
 }

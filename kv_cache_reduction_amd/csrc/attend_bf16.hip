@@ -44,6 +44,8 @@
 //    accumulator U[h, slot, cols] and (column group 0) m and the normaliser
 //    l of every head.  q is pre-scaled by scale*log2(e); exponentials use
 //    v_exp_f32.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -62,6 +64,7 @@ struct AttendBf16Params {
 constexpr float kRescaleSlack = 8.f;         // log2 units
 constexpr uint32_t kOutOfRange = 0x80000000u;  // byte offset beyond any buffer resource used here
 constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;  // two bf16 1.0
+constexpr uint32_t kQuietNaN = 0x7fc00000u;
 
 // q . k over 8 columns: q as packed bf16 hi/lo pairs (4 words each), k as
 // 8 bf16 in 4 words; two dot2 per column pair.
@@ -381,6 +384,291 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Exchange kernel (two equal column groups, dh = 128): each workgroup forms
+// the scores of its own 16 heads only, from its own columns, and the two
+// workgroups of a chunk swap them through memory.  K is then read once and
+// no score is computed twice.
+//
+// Scores of step j are formed kXchgLook steps ahead (in step j-3) and
+// published as 64-bit mailbox entries {tag, score}; tag = launch epoch and
+// step index, so a reader can tell a fresh entry from an old one without
+// any ordering between entries (relaxed agent-scope atomics: no fences, no
+// drain of the DMA queue).  In step i a wave
+//   1. checks the partner's entries of step i+1 (loaded by LDS DMA during
+//      step i-1) and copies them into the score buffer,
+//   2. starts the load of the partner's entries of step i+2,
+//   3. forms and publishes its own heads' scores of step i+3,
+//   4. reads the MFMA B operands of step i+1 and refills that ring slot with
+//      step i+5,
+//   5. runs the softmax and MFMAs of step i,
+// then the workgroup meets at a barrier.  Each wave's vector-memory queue
+// then holds, in order: poll(i+2), publish(i+3), 4 loads of step i+5, so
+// vmcnt(5) at the top of step i+1 means poll(i+2) has landed (and with it
+// the older ring loads).  A late partner is waited for with a bounded spin;
+// running out of it marks the piece's results NaN.  Both
+// workgroups of a pair must be resident together: the launch is cooperative.
+constexpr int kXchgLook = 3;
+constexpr int kMboxDepth = 8;                  // mailbox ring depth in steps
+constexpr uint32_t kPollSpinLimit = 1u << 14;  // re-polls before giving up
+
+struct XchgParams {
+  AttendBf16Params a;
+  unsigned long long* mbox;  // [nch][2][kMboxDepth][8 waves][16] {tag, score}
+  uint32_t epoch;            // 16 bits used
+};
+
+__device__ __forceinline__ void dma16_sc1(uint32_t lds, const i32x4& rsrc, uint32_t voff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+
+template <int NST>
+__global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
+  constexpr int DH = 128;
+  constexpr int LPS = 4;            // DMA instructions per step and wave (own unit only)
+  constexpr int SB = 4096;          // ring slot bytes per wave
+  constexpr int NS = 4;             // score buffers (steps i .. i+3)
+  static_assert(NST == 4, "ring: slots of steps i+1 .. i+4");
+  const AttendBf16Params& p = xp.a;
+  extern __shared__ __attribute__((aligned(16))) int smem[];
+  const int nw = blockDim.x >> 6;  // 8
+  char* ring = reinterpret_cast<char*>(smem);                                 // [nw][NST][SB]
+  float* S = reinterpret_cast<float*>(ring + (size_t)nw * NST * SB);           // [NS][32][8]
+  unsigned long long* pollbuf = reinterpret_cast<unsigned long long*>(S + NS * 256);  // [nw][2][16]
+  int* tmp = reinterpret_cast<int*>(pollbuf + nw * 32);                         // [16]
+  int* pre = tmp + 16;                                                          // [B+1]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  int c, cg;
+  {
+    const int bid = blockIdx.x;
+    if ((p.nch & 7) == 0) {  // the two workgroups of a chunk on one XCD
+      const int xcd = bid & 7, k = bid >> 3;
+      cg = k & 1;
+      c = ((k >> 1) << 3) + xcd;
+    } else {
+      c = bid >> 1;
+      cg = bid & 1;
+    }
+  }
+
+  for (int i = tid; i < NS * 256; i += blockDim.x) S[i] = kNegInf;
+  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);  // (ends with a barrier)
+  const int total = __builtin_amdgcn_readfirstlane(pre[p.B]);
+  if (total == 0) return;
+  const int Ts = chunk_tokens(total, p.nch);
+  const int cbeg = c * Ts;
+  if (cbeg >= total) return;
+  const int cend = min(total, cbeg + Ts);
+
+  const int d = p.d;
+  const int ubase = cg * p.dc + wave * kMfmaUnitCols;
+  const int ocol = ubase + 8 * l32;
+  const int xbase = (1 - cg) * p.dc + wave * kMfmaUnitCols;  // partner wave's unit
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const uint32_t step_bytes = row_bytes * kStepTokens;
+  const uint32_t vo = (uint32_t)(half * 4) * row_bytes + (uint32_t)ocol * 2u;
+  char* wring = ring + (size_t)wave * NST * SB;
+  const uint32_t wring_s = (uint32_t)reinterpret_cast<uintptr_t>(wring);
+  const uint4* rd16 = reinterpret_cast<const uint4*>(wring) + lane;
+  const int tr_off = ((lane & 15) >> 2) * 1024 + (lane >> 5) * 512 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  // mailbox entries: this wave publishes entry e = 8*(head within unit) + token
+  unsigned long long* mine = xp.mbox + ((size_t)(2 * c + cg) * kMboxDepth * 8 + wave) * 16;
+  const unsigned long long* theirs = xp.mbox + ((size_t)(2 * c + 1 - cg) * kMboxDepth * 8 + wave) * 16;
+  const uint32_t poll_lds = (uint32_t)reinterpret_cast<uintptr_t>(pollbuf + wave * 32);
+  const int r16 = lane & 15;
+  const int pub_e = (l32 >> 4) * 8 + half * 4 + 2 * (r16 & 1) + (r16 >> 1);  // valid for r16 < 4
+  const uint32_t ep = (xp.epoch & 0xffffu) << 16;
+  bool failed = false;
+
+  int gstep = 0;  // step counter across pieces (tags, score buffers)
+  for (int b = __builtin_amdgcn_readfirstlane(seq_of(pre, p.B, cbeg)); b < p.B; ++b) {
+    const int s0 = __builtin_amdgcn_readfirstlane(pre[b]), s1 = __builtin_amdgcn_readfirstlane(pre[b + 1]);
+    if (s0 >= cend) break;
+    if (s1 == s0) continue;
+    const int tb = max(cbeg, s0) - s0;
+    const int n = min(cend, s1) - s0 - tb;
+    const int slot = c + b;
+
+    uint4 qh, ql;
+    split_q8(p.q + (size_t)b * d + ocol, p.qscale, qh, ql);
+
+    const uint16_t* kbase = p.K + ((size_t)b * p.T_max + tb) * d;
+    const uint32_t nbytes = (uint32_t)n * row_bytes;
+    auto issue = [&](int step) {  // ring slot step % NST <- step
+      const uint32_t done = (uint32_t)step * step_bytes;
+      const uint32_t left = nbytes > done ? nbytes - done : 0u;
+      const i32x4 rs = buffer_desc(reinterpret_cast<const char*>(kbase) + (left ? done : 0u), left);
+      const uint32_t dst = wring_s + (step & (NST - 1)) * SB;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dma16(dst + k * 1024, rs, vo + k * row_bytes);
+    };
+    // own heads' scores of `step` -> S and the mailbox
+    auto publish = [&](int step) {
+      const int gs = gstep + step;
+      const int sl = step & (NST - 1);
+      uint4 ko[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ko[k] = rd16[(sl * SB + k * 1024) / 16];
+      float v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = dot8_split(qh, ql, ko[k]);
+      const float x = row16_sum4(v[0], v[1], v[2], v[3], lane);
+      if (r16 < 4) {
+        S[(gs & (NS - 1)) * 256 + (ocol / DH) * 8 + (pub_e & 7)] = x;
+        const unsigned long long ent =
+            ((unsigned long long)(ep | ((uint32_t)gs & 0xffffu)) << 32) | __float_as_uint(x);
+        __hip_atomic_store(mine + (size_t)(gs % kMboxDepth) * 8 * 16 + pub_e, ent, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    auto poll = [&](int step) {  // partner's entries of `step` -> pollbuf[step & 1]
+      const int gs = gstep + step;
+      if (lane < 8) {
+        const i32x4 rs = buffer_desc(theirs + (size_t)(gs % kMboxDepth) * 8 * 16, 128u);
+        dma16_sc1(poll_lds + (gs & 1) * 128, rs, 16u * lane);
+      }
+    };
+    // copy the partner's scores of `step` into S once all 16 entries carry
+    // the step's tag (the poll has landed); re-poll while they do not
+    auto check = [&](int step) {
+      const int gs = gstep + step;
+      const uint32_t want = ep | ((uint32_t)gs & 0xffffu);
+      uint32_t tries = 0;
+      while (true) {
+        const unsigned long long v = lane < 16 ? pollbuf[wave * 32 + (gs & 1) * 16 + lane] : 0ull;
+        const bool ok = lane >= 16 || (uint32_t)(v >> 32) == want;
+        if (__all(ok)) {
+          if (lane < 16) S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float((uint32_t)v);
+          break;
+        }
+        if (failed || ++tries > kPollSpinLimit) {
+          failed = true;
+          if (lane < 16) S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float(kQuietNaN);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+        wait_lgkmcnt0();
+        poll(step);
+        wait_vmcnt<0>();
+      }
+      wait_lgkmcnt0();  // the pollbuf read is done before the buffer is refilled
+    };
+    auto b_operands = [&](int step, s16x4 (&bop)[8]) {
+      const lds_s16x4* a0 =
+          (const lds_s16x4*)(size_t)(wring_s + (uint32_t)((step & (NST - 1)) * SB + tr_off));
+#pragma unroll
+      for (int s = 0; s < 8; ++s) bop[s] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(a0 + 8 * s));
+    };
+    auto barrier = [&]() {
+      wait_lgkmcnt0();
+      __builtin_amdgcn_s_barrier();
+    };
+
+    float m_ref = kNegInf, l_half = 0.f;
+    f32x16 acc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[s] = f32x16{0};
+    const int nsteps = (n + kStepTokens - 1) / kStepTokens;
+
+    // prologue: ring steps 0..3; scores of steps 0..2 published, the
+    // partner's of step 0 in S, its step 1 polled; B operands of step 0;
+    // step 4 in flight.  The queue ends with poll(1), publish(2), step 4.
+    s16x4 bcur[8];
+#pragma unroll
+    for (int s = 0; s < NST; ++s) issue(s);
+    wait_vmcnt<0>();
+    publish(0);
+    publish(1);
+    wait_lgkmcnt0();
+    poll(0);
+    wait_vmcnt<0>();
+    check(0);
+    poll(1);
+    publish(2);
+    b_operands(0, bcur);
+    wait_lgkmcnt0();
+    issue(NST);
+    barrier();
+
+    for (int st = 0; st < nsteps; ++st) {
+      wait_vmcnt<1 + LPS>();  // poll(st+1) and step st+3 have landed
+      check(st + 1);
+      poll(st + 2);
+      publish(st + 3);
+      s16x4 bnext[8];
+      b_operands(st + 1, bnext);
+      const float4 sv = *reinterpret_cast<const float4*>(S + ((gstep + st) & (NS - 1)) * 256 + l32 * 8 + half * 4);
+      float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+      if ((st + 1) * kStepTokens > n) {  // ragged last step
+        const int t0 = st * kStepTokens + half * 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sc[k] = t0 + k < n ? sc[k] : kNegInf;
+      }
+      wait_lgkmcnt0();
+      issue(st + 1 + NST);
+
+      float ma, mb;
+      halves(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), ma, mb);
+      const float mt = fmaxf(ma, mb);
+      const bool grow = mt > m_ref + kRescaleSlack;
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m_ref;
+        const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
+        l_half *= alpha;
+        m_ref = m_new;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float ar = __shfl(alpha, 8 * (e >> 2) + 4 * half + (e & 3), 64);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc[s][e] *= ar;
+        }
+      }
+      const float mu = fmaxf(m_ref, -__FLT_MAX__);
+      const bf16x2_t p01 = {(__bf16)fast_exp2(sc[0] - mu), (__bf16)fast_exp2(sc[1] - mu)};
+      const bf16x2_t p23 = {(__bf16)fast_exp2(sc[2] - mu), (__bf16)fast_exp2(sc[3] - mu)};
+      const uint32_t w0 = __builtin_bit_cast(uint32_t, p01);
+      const uint32_t w1 = __builtin_bit_cast(uint32_t, p23);
+      l_half = dot2_bf16(w1, kOnesBf16x2, dot2_bf16(w0, kOnesBf16x2, l_half));
+      {
+        uint2 aw = make_uint2(w0, w1);
+        const s16x4 a = __builtin_bit_cast(s16x4, aw);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bcur[s], acc[s], 0, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) bcur[s] = bnext[s];
+      barrier();
+    }
+    gstep += nsteps + kXchgLook;
+    wait_vmcnt<0>();
+
+    float la, lb;
+    halves(l_half, la, lb);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+      if (row < p.H) {
+        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ubase + l32;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) dst[32 * s] = acc[s][e];
+      }
+    }
+    if (cg == 0 && wave == 0 && lane < p.H) {
+      p.ml[(size_t)slot * 2 * p.H + lane] = failed ? __uint_as_float(kQuietNaN) : m_ref;
+      p.ml[(size_t)slot * 2 * p.H + p.H + lane] = la + lb;
+    }
+  }
+}
+
 template <int DH, int GC>
 static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = GC == 2 ? 2 : 4;
@@ -412,7 +700,65 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   return hipGetLastError();
 }
 
+// Per-launch epoch of the mailbox tags: distinct for consecutive launches of
+// the process.
+static uint32_t next_epoch() {
+  static std::atomic<uint32_t> ctr{0x5a17u};
+  return ctr.fetch_add(1) + 1;
+}
+
+// Launches the exchange kernel when the shape allows it (two full column
+// groups of dh = 128) and the device runs the whole grid at once; returns
+// hipErrorNotSupported otherwise, and the caller falls back.
+static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
+  constexpr int NST = 4;
+  if (!pl.xchg || env_int("SLIM_XCHG", 1) == 0) return hipErrorNotSupported;
+  XchgParams xp;
+  AttendBf16Params& p = xp.a;
+  p.q = a.q;
+  p.K = static_cast<const uint16_t*>(a.K);
+  p.lengths = a.lengths;
+  p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
+  p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
+  p.B = a.B;
+  p.H = a.H;
+  p.d = a.d;
+  p.T_max = a.T_max;
+  p.nch = pl.nch;
+  p.dc = pl.dc;
+  p.nslots = pl.nslots;
+  p.qscale = a.scale * kLog2e;
+  xp.mbox = reinterpret_cast<unsigned long long*>(a.ws + pl.off_mbox);
+  xp.epoch = next_epoch();
+  const size_t lds = (size_t)pl.nw * NST * 4096 + 4 * 256 * sizeof(float) +
+                     (size_t)pl.nw * 32 * sizeof(unsigned long long) + (16 + (size_t)a.B + 1) * sizeof(int);
+  auto kern = attend_xchg_kernel<NST>;
+  static int lds_allowed = 0;
+  if ((int)lds > lds_allowed) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess) {
+      (void)hipGetLastError();
+      return hipErrorNotSupported;
+    }
+    lds_allowed = (int)lds;
+  }
+  // the workgroups of a pair wait on each other: a cooperative launch
+  // guarantees they are resident together (or refuses the launch)
+  void* args[] = {&xp};
+  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(pl.nch * 2),
+                                            dim3(pl.nw * 64), args, (unsigned)lds, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_attend_bf16(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
+  if (pl.gc == 2 && a.dh == 128) {
+    const hipError_t e = launch_xchg(pl, a, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (pl.gc == 1) {
     switch (a.dh) {
       case 32: return launch_t<32, 1>(pl, a, s);

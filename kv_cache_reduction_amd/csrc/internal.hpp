@@ -23,6 +23,8 @@ struct DecodePlan {
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
   size_t off_u;    // [B, H, d] float: merged softmax.K rows
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
+  bool xchg;       // two equal column groups whose workgroups exchange scores
+  size_t off_mbox; // [nch, 2, 8, 8, 16] u64 score mailboxes of the exchange
   size_t bytes;
 };
 

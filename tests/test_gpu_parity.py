@@ -253,3 +253,21 @@ def test_two_column_groups_ragged_with_empty_sequence():
     ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
     assert np.all(o[2] == 0)
     _check("two column groups", o, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("xchg", ["1", "0"])
+def test_score_exchange_and_fallback(monkeypatch, xchg):
+    """The exchange kernel (each column group forms its own heads' scores and
+    the pair swaps them) and the kernel that forms all scores in both
+    workgroups, on a 7B-shaped ragged batch with several pieces per chunk."""
+    monkeypatch.setenv("SLIM_XCHG", xchg)
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=6, T_max=3000, len_lo=1, len_hi=3000)
+    wl = syn.make(cfg)
+    lens = wl.lengths.copy()
+    lens[3] = 0
+    lens[4] = 1
+    K = syn.k_cache(cfg, wl.w, np.minimum(lens, cfg.T_max))
+    o = gpu_decode(cfg, wl.q, to_dev(K), lens, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
+    assert np.all(o[3] == 0)
+    _check(f"xchg={xchg}", o, ref, TOL["bf16"])
