@@ -85,6 +85,8 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   p->xchg = bf16_k && p->gc == 2 && dh == 128 && 2 * p->dc == d && p->nw == 8;
   p->off_mbox = off;
   off += p->xchg ? align256((size_t)p->nch * 2 * 8 * 8 * 16 * sizeof(unsigned long long)) : 0;
+  p->off_tickets = off;
+  off += 256;
   p->bytes = off;
   return true;
 }

@@ -406,15 +406,17 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
 // then holds, in order: poll(i+2), publish(i+3), 4 loads of step i+5, so
 // vmcnt(5) at the top of step i+1 means poll(i+2) has landed (and with it
 // the older ring loads).  A late partner is waited for with a bounded spin;
-// running out of it marks the piece's results NaN.  Both
-// workgroups of a pair must be resident together: the launch is cooperative.
+// running out of it marks the piece's results NaN.  Workgroups take their
+// roles in arrival order (see the kernel), so the two of a pair are
+// resident together without a cooperative launch.
 constexpr int kXchgLook = 3;
 constexpr int kMboxDepth = 8;                  // mailbox ring depth in steps
-constexpr uint32_t kPollSpinLimit = 1u << 14;  // re-polls before giving up
+constexpr uint32_t kPollSpinLimit = 1u << 19;  // re-polls (about a second) before giving up
 
 struct XchgParams {
   AttendBf16Params a;
-  unsigned long long* mbox;  // [nch][2][kMboxDepth][8 waves][16] {tag, score}
+  unsigned long long* mbox;     // [nch][2][kMboxDepth][8 waves][16] {tag, score}
+  unsigned long long* tickets;  // arrival counter (any initial value)
   uint32_t epoch;            // 16 bits used
 };
 
@@ -447,21 +449,19 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  int c, cg;
-  {
-    const int bid = blockIdx.x;
-    if ((p.nch & 7) == 0) {  // the two workgroups of a chunk on one XCD
-      const int xcd = bid & 7, k = bid >> 3;
-      cg = k & 1;
-      c = ((k >> 1) << 3) + xcd;
-    } else {
-      c = bid >> 1;
-      cg = bid & 1;
-    }
-  }
-
+  // Roles by arrival: role = (ticket mod grid size); roles 2c and 2c+1 form
+  // chunk c's pair.  Any gridDim.x consecutive tickets cover every role
+  // once, whatever the counter held before, and a workgroup's partner is
+  // the next or previous arrival (one pair wraps from the first arrival to
+  // the last), so a resident workgroup never waits on one that cannot be
+  // scheduled.
+  if (tid == 0)
+    tmp[15] = (int)(__hip_atomic_fetch_add(xp.tickets, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) %
+                    (unsigned long long)gridDim.x);
   for (int i = tid; i < NS * 256; i += blockDim.x) S[i] = kNegInf;
-  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);  // (ends with a barrier)
+  lengths_prefix(p.lengths, p.B, p.T_max, pre, tmp);  // (ends with a barrier; leaves tmp[15])
+  const int role = __builtin_amdgcn_readfirstlane(tmp[15]);
+  const int c = role >> 1, cg = role & 1;
   const int total = __builtin_amdgcn_readfirstlane(pre[p.B]);
   if (total == 0) return;
   const int Ts = chunk_tokens(total, p.nch);
@@ -708,8 +708,8 @@ static uint32_t next_epoch() {
 }
 
 // Launches the exchange kernel when the shape allows it (two full column
-// groups of dh = 128) and the device runs the whole grid at once; returns
-// hipErrorNotSupported otherwise, and the caller falls back.
+// groups of dh = 128); returns hipErrorNotSupported otherwise, and the caller
+// falls back.
 static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = 4;
   if (!pl.xchg || env_int("SLIM_XCHG", 1) == 0) return hipErrorNotSupported;
@@ -729,6 +729,7 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
   xp.mbox = reinterpret_cast<unsigned long long*>(a.ws + pl.off_mbox);
+  xp.tickets = reinterpret_cast<unsigned long long*>(a.ws + pl.off_tickets);
   xp.epoch = next_epoch();
   const size_t lds = (size_t)pl.nw * NST * 4096 + 4 * 256 * sizeof(float) +
                      (size_t)pl.nw * 32 * sizeof(unsigned long long) + (16 + (size_t)a.B + 1) * sizeof(int);
@@ -742,16 +743,8 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
     }
     lds_allowed = (int)lds;
   }
-  // the workgroups of a pair wait on each other: a cooperative launch
-  // guarantees they are resident together (or refuses the launch)
-  void* args[] = {&xp};
-  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(pl.nch * 2),
-                                            dim3(pl.nw * 64), args, (unsigned)lds, s);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return hipErrorNotSupported;
-  }
-  return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(pl.nch * 2), dim3(pl.nw * 64), lds, s, xp);
+  return hipGetLastError();
 }
 
 hipError_t launch_attend_bf16(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {

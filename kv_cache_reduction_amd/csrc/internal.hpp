@@ -25,6 +25,7 @@ struct DecodePlan {
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
   bool xchg;       // two equal column groups whose workgroups exchange scores
   size_t off_mbox; // [nch, 2, 8, 8, 16] u64 score mailboxes of the exchange
+  size_t off_tickets;  // u64 arrival counter of the exchange workgroups
   size_t bytes;
 };
 
