@@ -179,6 +179,16 @@ def measured_traffic(kernel_sources):
     return rec.get("hbm_bytes_per_launch")
 
 
+def attend_kernel_name(cfg):
+    """The attend kernel the library picks for this shape: the score
+    exchange between the two column groups for d = 2*dc with dh = 128 (d a
+    multiple of 512 above 2048), the one-workgroup-per-column-group kernel
+    otherwise."""
+    xchg = (cfg.dh == 128 and cfg.d > 2048 and cfg.d % 512 == 0
+            and os.environ.get("SLIM_XCHG", "1") != "0")
+    return "slim::attend_xchg_kernel<4>" if xchg else "slim::attend_bf16_kernel"
+
+
 def probe_read_gbps(torch, slim, src):
     sink = torch.empty(slim.probe_sink_floats(), dtype=torch.float32, device="cuda")
     for _ in range(3):
@@ -291,7 +301,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": k_gbps_attend, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": k_gbps_attend / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(ATTEND_SOURCES) if name == "c3" else None,
-                     "kernel": "attend_bf16_kernel", "kernel_us": att_ms * 1e3,
+                     "kernel": attend_kernel_name(cfg), "kernel_us": att_ms * 1e3,
                      "algorithmic_bytes": wl.k_bytes},
     }
 

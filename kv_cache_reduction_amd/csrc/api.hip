@@ -78,8 +78,6 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   off += align256((size_t)p->nslots * H * d * sizeof(float));
   p->off_ml = off;
   off += align256((size_t)p->nslots * 2 * H * sizeof(float));
-  p->off_u = off;
-  off += align256((size_t)B * H * d * sizeof(float));
   p->off_op = off;
   off += align256((size_t)p->npc * B * H * dh * sizeof(float));
   p->xchg = bf16_k && p->gc == 2 && dh == 128 && 2 * p->dc == d && p->nw == 8;

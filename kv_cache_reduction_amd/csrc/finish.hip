@@ -6,15 +6,15 @@
 // Partials (written by the attend phase) are laid out U[h][slot][d] and
 // ml[slot][2][H] (running max in log2 units, normaliser).
 //
-// combine  grid (H, d/512, B): for sequence b with slots s (log-sum-exp merge)
+// merge_project  grid (H, ceil(d/R), ceil(B/8)), R = proj_rows(dh) rows of
+//          W_KV per workgroup.  For each of its (up to 8) sequences b the
+//          workgroup first merges the slots s of b over its R rows
+//          (log-sum-exp):
 //            m* = max_s m_s,  l* = sum_s 2^(m_s - m*) l_s,
-//            u[b, h, c] = sum_s 2^(m_s - m*) U_s[h, c] / l*
-//          Each thread sums one float4 of columns over a strided subset of the
-//          slots; the subsets meet in LDS.
-// project  grid (H, d/R, ceil(B/8)) with R = proj_rows(dh): the workgroup
-//          holds W_KV[R rows, h-slice] in registers (16-byte loads) and forms
-//          the partial products of up to 8 sequences:
-//            part[rb, b, h, j] = sum_{c in rows} u[b, h, c] W_KV[c, h*dh + j]
+//            u[r] = sum_s 2^(m_s - m*) U_s[h, r] / l*,
+//          then multiplies by the W_KV rows it holds in registers:
+//            part[rb, b, h, j] = sum_{r in rows} u[r] W_KV[r, h*dh + j].
+//          The partials are read once and W_KV once per 8 sequences.
 // reduce   out[b, h, j] = sum_rb part[rb, b, h, j] in a fixed order, so the
 //          result does not depend on scheduling.
 #include "common.hpp"
@@ -22,102 +22,41 @@
 
 namespace slim {
 
-constexpr int kCombineCols = 512;  // columns per combine workgroup (128 threads x float4)
-constexpr int kSeqPerProj = 8;     // sequences per projection workgroup
-
-__global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ lengths,
-                                                      const float* __restrict__ U,
-                                                      const float* __restrict__ ml,
-                                                      float* __restrict__ u_out, int B, int H, int d,
-                                                      int T_max, int nch, int nslots) {
-  extern __shared__ int smem[];
-  int* tmp = smem;                                   // [8]
-  float* red = reinterpret_cast<float*>(smem + 8);   // [2][kCombineCols]
-  float* wts = red + 2 * kCombineCols;               // [nch + 1]
-  int* pre = reinterpret_cast<int*>(wts + nch + 1);  // [B + 1]
-  const int tid = threadIdx.x;
-  const int h = blockIdx.x, c0 = blockIdx.y * kCombineCols, b = blockIdx.z;
-
-  lengths_prefix(lengths, B, T_max, pre, tmp);
-  const int s0 = pre[b], s1 = pre[b + 1];
-  float* dst = u_out + ((size_t)b * H + h) * d + c0;
-  const int ncols = min(kCombineCols, d - c0);
-  if (s1 == s0) {
-    for (int i = tid; i < ncols; i += blockDim.x) dst[i] = 0.f;
-    return;
-  }
-  const int Ts = chunk_tokens(pre[B], nch);
-  const int cf = s0 / Ts, cl = (s1 - 1) / Ts, ns = cl - cf + 1, slot0 = cf + b;
-
-  if (tid < 64) {  // slot weights 2^(m_s - m*) / l*, one wave
-    float m = kNegInf;
-    for (int i = tid; i < ns; i += 64) m = fmaxf(m, ml[(size_t)(slot0 + i) * 2 * H + h]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float l = 0.f;
-    for (int i = tid; i < ns; i += 64) {
-      const float* e = ml + (size_t)(slot0 + i) * 2 * H;
-      const float w = fast_exp2(e[h] - m);
-      wts[i] = w;
-      l += w * e[H + h];
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    const float inv = 1.f / l;
-    for (int i = tid; i < ns; i += 64) wts[i] *= inv;
-  }
-  __syncthreads();
-
-  const int j4 = tid & 127, g = tid >> 7;  // 128 float4 columns x 2 slot subsets
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* src = U + ((size_t)h * nslots + slot0) * d + c0 + 4 * j4;
-  if ((d & 3) == 0 && 4 * j4 < ncols) {
-#pragma unroll 16
-    for (int i = g; i < ns; i += 2) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (size_t)i * d);
-      const float w = wts[i];
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
-    }
-  } else if (4 * j4 < ncols) {  // rows not 16-byte aligned (d % 4 != 0)
-    for (int i = g; i < ns; i += 2) {
-      const float* v = src + (size_t)i * d;
-      const float w = wts[i];
-      acc.x = fmaf(w, v[0], acc.x);
-      if (4 * j4 + 1 < ncols) acc.y = fmaf(w, v[1], acc.y);
-      if (4 * j4 + 2 < ncols) acc.z = fmaf(w, v[2], acc.z);
-      if (4 * j4 + 3 < ncols) acc.w = fmaf(w, v[3], acc.w);
-    }
-  }
-  float* r = red + g * kCombineCols + 4 * j4;
-  r[0] = acc.x;
-  r[1] = acc.y;
-  r[2] = acc.z;
-  r[3] = acc.w;
-  __syncthreads();
-  for (int i = tid; i < ncols; i += blockDim.x) dst[i] = red[i] + red[kCombineCols + i];
-}
+constexpr int kSeqPerProj = 8;  // sequences per workgroup
 
 template <int DH, bool WBF16>
-__global__ void __launch_bounds__(256) project_kernel(const float* __restrict__ u,
-                                                      const void* __restrict__ W,
-                                                      float* __restrict__ part, int B, int H, int d) {
-  // thread t: JW output columns (group jq = t % JQ) over the rows of subset t / JQ
+__global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __restrict__ lengths,
+                                                            const float* __restrict__ U,
+                                                            const float* __restrict__ ml,
+                                                            const void* __restrict__ W,
+                                                            float* __restrict__ part, int B, int H, int d,
+                                                            int T_max, int nch, int nslots) {
+  // projection: thread t covers JW output columns (group jq = t % JQ) over the
+  // rows of subset t / JQ
   constexpr int PR = proj_rows(DH);
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;  // column groups per head
   constexpr int JW = DH >= 8 ? 8 : DH;      // columns per group
   constexpr int NRS = 256 / JQ;             // row subsets
   constexpr int RPT = PR / NRS;             // rows per thread
   static_assert(RPT >= 1 && RPT * NRS == PR, "row split");
-  __shared__ float red[NRS * DH];
-  __shared__ float us[kSeqPerProj][PR];
-  const int tid = threadIdx.x;
+  // merge: thread t sums float4 column t % C4 over the slot subset t / C4
+  constexpr int C4 = PR / 4;
+  constexpr int NSS = 256 / C4;
+  static_assert(C4 * NSS == 256, "merge split");
+  extern __shared__ int smem[];
+  int* tmp = smem;                                       // [8]
+  float* red = reinterpret_cast<float*>(smem + 8);       // [max(NSS * PR, NRS * DH)]
+  constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
+  float* us = red + RED;                                 // [8][PR]
+  float* mstar = us + kSeqPerProj * PR;                  // [8][2]: m*, 1/l*
+  int* pre = reinterpret_cast<int*>(mstar + 2 * kSeqPerProj);  // [B + 1]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * kSeqPerProj;
   const int nr = min(PR, d - r0), nb = min(kSeqPerProj, B - b0);
-  const int jq = tid % JQ, rs = tid / JQ;
 
+  // W_KV rows [r0, r0 + PR) of head h's columns, in registers
+  const int jq = tid % JQ, rs = tid / JQ;
   float w[RPT][JW];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -140,11 +79,78 @@ __global__ void __launch_bounds__(256) project_kernel(const float* __restrict__ 
       for (int k = 0; k < JW; ++k) w[i][k] = 0.f;
     }
   }
-  for (int i = tid; i < nb * PR; i += 256) {
-    const int bb = i / PR, r = i % PR;
-    us[bb][r] = r < nr ? u[((size_t)(b0 + bb) * H + h) * d + r0 + r] : 0.f;
+
+  lengths_prefix(lengths, B, T_max, pre, tmp);
+  const int Ts = chunk_tokens(pre[B] > 0 ? pre[B] : 1, nch);
+
+  // m* and 1/l* of each sequence of the group, one wave per sequence
+  for (int bb = wave; bb < nb; bb += 4) {
+    const int b = b0 + bb;
+    const int s0 = pre[b], s1 = pre[b + 1];
+    float m = kNegInf, l = 0.f;
+    if (s1 > s0) {
+      const int cf = s0 / Ts, ns = (s1 - 1) / Ts - cf + 1, slot0 = cf + b;
+      for (int i = lane; i < ns; i += 64) m = fmaxf(m, ml[(size_t)(slot0 + i) * 2 * H + h]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      for (int i = lane; i < ns; i += 64) {
+        const float* e = ml + (size_t)(slot0 + i) * 2 * H;
+        l += fast_exp2(e[h] - m) * e[H + h];
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    }
+    if (lane == 0) {
+      mstar[2 * bb] = m;
+      mstar[2 * bb + 1] = l > 0.f ? 1.f / l : 0.f;
+    }
   }
   __syncthreads();
+
+  // merged rows u[bb][r] of head h, rows [r0, r0 + nr)
+  const int c4 = tid % C4, ss = tid / C4;
+  const bool aligned = (d & 3) == 0;
+  for (int bb = 0; bb < nb; ++bb) {
+    const int b = b0 + bb;
+    const int s0 = pre[b], s1 = pre[b + 1];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s1 > s0 && 4 * c4 < nr) {
+      const int cf = s0 / Ts, ns = (s1 - 1) / Ts - cf + 1, slot0 = cf + b;
+      const float m = mstar[2 * bb], il = mstar[2 * bb + 1];
+      const float* src = U + ((size_t)h * nslots + slot0) * d + r0 + 4 * c4;
+      for (int i = ss; i < ns; i += NSS) {
+        const float wt = fast_exp2(ml[(size_t)(slot0 + i) * 2 * H + h] - m) * il;
+        const float* v = src + (size_t)i * d;
+        if (aligned) {
+          const float4 x = *reinterpret_cast<const float4*>(v);
+          acc.x = fmaf(wt, x.x, acc.x);
+          acc.y = fmaf(wt, x.y, acc.y);
+          acc.z = fmaf(wt, x.z, acc.z);
+          acc.w = fmaf(wt, x.w, acc.w);
+        } else {  // rows not 16-byte aligned (d % 4 != 0)
+          acc.x = fmaf(wt, v[0], acc.x);
+          if (4 * c4 + 1 < nr) acc.y = fmaf(wt, v[1], acc.y);
+          if (4 * c4 + 2 < nr) acc.z = fmaf(wt, v[2], acc.z);
+          if (4 * c4 + 3 < nr) acc.w = fmaf(wt, v[3], acc.w);
+        }
+      }
+    }
+    float* rr = red + ss * PR + 4 * c4;
+    rr[0] = acc.x;
+    rr[1] = acc.y;
+    rr[2] = acc.z;
+    rr[3] = acc.w;
+    __syncthreads();
+    for (int r = tid; r < PR; r += 256) {
+      float x = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < NSS; ++k) x += red[k * PR + r];
+      us[bb * PR + r] = r < nr ? x : 0.f;
+    }
+    __syncthreads();
+  }
+
+  // projection of each merged row block by the W_KV rows held in registers
   const size_t nout = (size_t)B * H * DH;
   for (int bb = 0; bb < nb; ++bb) {
     float acc[JW];
@@ -152,18 +158,18 @@ __global__ void __launch_bounds__(256) project_kernel(const float* __restrict__ 
     for (int k = 0; k < JW; ++k) acc[k] = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const float x = us[bb][rs * RPT + i];
+      const float x = us[bb * PR + rs * RPT + i];
 #pragma unroll
       for (int k = 0; k < JW; ++k) acc[k] = fmaf(x, w[i][k], acc[k]);
     }
 #pragma unroll
     for (int k = 0; k < JW; ++k) red[rs * DH + jq * JW + k] = acc[k];
     __syncthreads();
-    if (tid < DH) {
+    for (int j = tid; j < DH; j += 256) {
       float s = 0.f;
 #pragma unroll 8
-      for (int k = 0; k < NRS; ++k) s += red[k * DH + tid];
-      part[(size_t)blockIdx.y * nout + ((size_t)(b0 + bb) * H + h) * DH + tid] = s;
+      for (int k = 0; k < NRS; ++k) s += red[k * DH + j];
+      part[(size_t)blockIdx.y * nout + ((size_t)(b0 + bb) * H + h) * DH + j] = s;
     }
     __syncthreads();
   }
@@ -181,19 +187,19 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(const float* __restric
 
 template <int DH, bool WBF16>
 static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
+  constexpr int PR = proj_rows(DH);
+  constexpr int JQ = DH >= 8 ? DH / 8 : 1;
+  constexpr int NRS = 256 / JQ;
+  constexpr int NSS = 256 / (PR / 4);
+  constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
   const float* U = reinterpret_cast<const float*>(a.ws + pl.off_U);
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
-  float* uo = reinterpret_cast<float*>(a.ws + pl.off_u);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
-  const size_t lds = (8 + 2 * kCombineCols + (size_t)pl.nch + 1 + (size_t)a.B + 1) * 4;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.H, (a.d + kCombineCols - 1) / kCombineCols, a.B), dim3(256),
-                     lds, s, a.lengths, U, ml, uo, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots);
+  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * kSeqPerProj + (size_t)a.B + 1) * 4;
+  hipLaunchKernelGGL((merge_project_kernel<DH, WBF16>),
+                     dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), lds, s, a.lengths,
+                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((project_kernel<DH, WBF16>),
-                     dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), 0, s,
-                     (const float*)uo, a.W, part, a.B, a.H, a.d);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;
   hipLaunchKernelGGL(proj_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, (const float*)part,

@@ -21,7 +21,6 @@ struct DecodePlan {
   int npc;         // W_KV row blocks of the projection (proj_rows(dh) rows each)
   size_t off_U;    // [H, nslots, d] float: unnormalised softmax.K rows per chunk
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
-  size_t off_u;    // [B, H, d] float: merged softmax.K rows
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
   bool xchg;       // two equal column groups whose workgroups exchange scores
   size_t off_mbox; // [nch, 2, 8, 8, 16] u64 score mailboxes of the exchange
@@ -41,8 +40,9 @@ struct DecodeArgs {
   char* ws;
 };
 
-// W_KV rows per projection workgroup (keeps the per-thread slice <= 64 values)
-constexpr int proj_rows(int dh) { return dh > 128 ? 64 : 256; }
+// W_KV rows per finish workgroup: a multiple of the projection's row subsets
+// (256 threads / (dh/8) column groups) and of 64
+constexpr int proj_rows(int dh) { return dh >= 32 ? 64 : (dh >= 16 ? 128 : 256); }
 constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
 constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)
 
