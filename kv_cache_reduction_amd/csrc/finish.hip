@@ -11,7 +11,9 @@
 //          workgroup first merges the slots s of b over its R rows
 //          (log-sum-exp):
 //            m* = max_s m_s,  l* = sum_s 2^(m_s - m*) l_s,
-//            u[r] = sum_s 2^(m_s - m*) U_s[h, r] / l*,
+//            u[r] = sum_s 2^(m_s - m*) U_s[h, r] / l*
+//          (each thread over its own slots with a running max, then the
+//          threads' sums combined the same way),
 //          then multiplies by the W_KV rows it holds in registers:
 //            part[rb, b, h, j] = sum_{r in rows} u[r] W_KV[r, h*dh + j].
 //          The partials are read once and W_KV once per 8 sequences.
@@ -39,7 +41,8 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   constexpr int NRS = 256 / JQ;             // row subsets
   constexpr int RPT = PR / NRS;             // rows per thread
   static_assert(RPT >= 1 && RPT * NRS == PR, "row split");
-  // merge: thread t sums float4 column t % C4 over the slot subset t / C4
+  // merge: float4 column c4 of a slot subset; 256 / C4 (sequence, subset)
+  // pairs share the workgroup
   constexpr int C4 = PR / 4;
   constexpr int NSS = 256 / C4;
   static_assert(C4 * NSS == 256, "merge split");
@@ -48,8 +51,8 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   float* red = reinterpret_cast<float*>(smem + 8);       // [max(NSS * PR, NRS * DH)]
   constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
   float* us = red + RED;                                 // [8][PR]
-  float* mstar = us + kSeqPerProj * PR;                  // [8][2]: m*, 1/l*
-  int* pre = reinterpret_cast<int*>(mstar + 2 * kSeqPerProj);  // [B + 1]
+  float* mstar = us + kSeqPerProj * PR;                  // [NSS][2]: running max, normaliser
+  int* pre = reinterpret_cast<int*>(mstar + 2 * NSS);    // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * kSeqPerProj;
@@ -83,69 +86,98 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   lengths_prefix(lengths, B, T_max, pre, tmp);
   const int Ts = chunk_tokens(pre[B] > 0 ? pre[B] : 1, nch);
 
-  // m* and 1/l* of each sequence of the group, one wave per sequence
-  for (int bb = wave; bb < nb; bb += 4) {
-    const int b = b0 + bb;
-    const int s0 = pre[b], s1 = pre[b + 1];
-    float m = kNegInf, l = 0.f;
-    if (s1 > s0) {
-      const int cf = s0 / Ts, ns = (s1 - 1) / Ts - cf + 1, slot0 = cf + b;
-      for (int i = lane; i < ns; i += 64) m = fmaxf(m, ml[(size_t)(slot0 + i) * 2 * H + h]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      for (int i = lane; i < ns; i += 64) {
-        const float* e = ml + (size_t)(slot0 + i) * 2 * H;
-        l += fast_exp2(e[h] - m) * e[H + h];
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    }
-    if (lane == 0) {
-      mstar[2 * bb] = m;
-      mstar[2 * bb + 1] = l > 0.f ? 1.f / l : 0.f;
-    }
-  }
-  __syncthreads();
-
-  // merged rows u[bb][r] of head h, rows [r0, r0 + nr)
-  const int c4 = tid % C4, ss = tid / C4;
+  // merged rows u[bb][r] of head h, rows [r0, r0 + nr): G sequences at a
+  // time, 256/G threads each (C4 float4 columns x nss slot subsets).  Each
+  // thread merges its slots with a running max of its own (one pass over U
+  // and ml); the subsets then meet in LDS with the usual rescaling.
+  int G = nb >= 8 ? 8 : (nb >= 4 ? 4 : (nb >= 2 ? 2 : 1));
+  if (G > NSS) G = NSS;
+  const int tps = 256 / G, nss = tps / C4;
+  const int g = tid / tps, c4 = (tid % tps) % C4, ss = (tid % tps) / C4;
   const bool aligned = (d & 3) == 0;
-  for (int bb = 0; bb < nb; ++bb) {
+  for (int base = 0; base < nb; base += G) {
+    const int bb = base + g;
     const int b = b0 + bb;
-    const int s0 = pre[b], s1 = pre[b + 1];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (s1 > s0 && 4 * c4 < nr) {
+    float m = kNegInf, l = 0.f;
+    bool bad = false;
+    if (bb < nb && pre[b + 1] > pre[b]) {
+      const int s0 = pre[b], s1 = pre[b + 1];
       const int cf = s0 / Ts, ns = (s1 - 1) / Ts - cf + 1, slot0 = cf + b;
-      const float m = mstar[2 * bb], il = mstar[2 * bb + 1];
+      const bool cols = 4 * c4 < nr;
       const float* src = U + ((size_t)h * nslots + slot0) * d + r0 + 4 * c4;
-      for (int i = ss; i < ns; i += NSS) {
-        const float wt = fast_exp2(ml[(size_t)(slot0 + i) * 2 * H + h] - m) * il;
-        const float* v = src + (size_t)i * d;
-        if (aligned) {
-          const float4 x = *reinterpret_cast<const float4*>(v);
-          acc.x = fmaf(wt, x.x, acc.x);
-          acc.y = fmaf(wt, x.y, acc.y);
-          acc.z = fmaf(wt, x.z, acc.z);
-          acc.w = fmaf(wt, x.w, acc.w);
-        } else {  // rows not 16-byte aligned (d % 4 != 0)
-          acc.x = fmaf(wt, v[0], acc.x);
-          if (4 * c4 + 1 < nr) acc.y = fmaf(wt, v[1], acc.y);
-          if (4 * c4 + 2 < nr) acc.z = fmaf(wt, v[2], acc.z);
-          if (4 * c4 + 3 < nr) acc.w = fmaf(wt, v[3], acc.w);
+      const float* mls = ml + (size_t)slot0 * 2 * H + h;
+      for (int i = ss; i < ns; i += 4 * nss) {  // four slots per round, loads first
+        float4 x[4];
+        float ms[4], ls[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int j = i + k * nss;
+          const bool ok = j < ns;
+          ms[k] = ok ? mls[(size_t)j * 2 * H] : kNegInf;
+          ls[k] = ok ? mls[(size_t)j * 2 * H + H] : 0.f;
+          x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (ok && cols) {
+            const float* v = src + (size_t)j * d;
+            if (aligned) {
+              x[k] = *reinterpret_cast<const float4*>(v);
+            } else {  // rows not 16-byte aligned (d % 4 != 0)
+              x[k].x = v[0];
+              if (4 * c4 + 1 < nr) x[k].y = v[1];
+              if (4 * c4 + 2 < nr) x[k].z = v[2];
+              if (4 * c4 + 3 < nr) x[k].w = v[3];
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bad |= ms[k] != ms[k];  // an attend piece marked NaN
+        const float mn = fmaxf(fmaxf(m, fmaxf(ms[0], ms[1])), fmaxf(ms[2], ms[3]));
+        if (mn > kNegInf) {
+          const float sc = fast_exp2(m - mn);
+          acc.x *= sc;
+          acc.y *= sc;
+          acc.z *= sc;
+          acc.w *= sc;
+          l *= sc;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float q = fast_exp2(ms[k] - mn);
+            l = fmaf(q, ls[k], l);
+            acc.x = fmaf(q, x[k].x, acc.x);
+            acc.y = fmaf(q, x[k].y, acc.y);
+            acc.z = fmaf(q, x[k].z, acc.z);
+            acc.w = fmaf(q, x[k].w, acc.w);
+          }
+          m = mn;
         }
       }
     }
-    float* rr = red + ss * PR + 4 * c4;
+    const int slot_id = g * nss + ss;  // < NSS
+    float* rr = red + slot_id * PR + 4 * c4;
     rr[0] = acc.x;
     rr[1] = acc.y;
     rr[2] = acc.z;
     rr[3] = acc.w;
+    if (c4 == 0) {
+      mstar[2 * slot_id] = m;
+      mstar[2 * slot_id + 1] = bad ? __builtin_nanf("") : l;
+    }
     __syncthreads();
-    for (int r = tid; r < PR; r += 256) {
-      float x = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < NSS; ++k) x += red[k * PR + r];
-      us[bb * PR + r] = r < nr ? x : 0.f;
+    for (int r = tid; r < G * PR; r += 256) {
+      const int gg = r / PR, rw = r % PR;
+      float mx = kNegInf;
+      for (int k = 0; k < nss; ++k) mx = fmaxf(mx, mstar[2 * (gg * nss + k)]);
+      float x = 0.f, lt = 0.f;
+      for (int k = 0; k < nss; ++k)
+        if (mstar[2 * (gg * nss + k) + 1] != mstar[2 * (gg * nss + k) + 1]) lt = __builtin_nanf("");
+      if (mx > kNegInf) {
+        for (int k = 0; k < nss; ++k) {
+          const float q = fast_exp2(mstar[2 * (gg * nss + k)] - mx);
+          x = fmaf(q, red[(gg * nss + k) * PR + rw], x);
+          lt = fmaf(q, mstar[2 * (gg * nss + k) + 1], lt);
+        }
+      }
+      if (base + gg < nb) us[(base + gg) * PR + rw] = (rw < nr && !(lt <= 0.f)) ? x / lt : 0.f;
     }
     __syncthreads();
   }
@@ -195,7 +227,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   const float* U = reinterpret_cast<const float*>(a.ws + pl.off_U);
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
-  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * kSeqPerProj + (size_t)a.B + 1) * 4;
+  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * NSS + (size_t)a.B + 1) * 4;
   hipLaunchKernelGGL((merge_project_kernel<DH, WBF16>),
                      dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), lds, s, a.lengths,
                      U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots);
