@@ -41,8 +41,9 @@ struct DecodeArgs {
 };
 
 // W_KV rows per finish workgroup: a multiple of the projection's row subsets
-// (256 threads / (dh/8) column groups) and of 64
-constexpr int proj_rows(int dh) { return dh >= 32 ? 64 : (dh >= 16 ? 128 : 256); }
+// (256 threads / (dh/8) column groups); 256 rows (1 KB of a partial row per
+// slot) measured fastest for the merge, 64 keeps dh = 256 out of spills
+constexpr int proj_rows(int dh) { return dh > 128 ? 64 : 256; }
 constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
 constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)
 
