@@ -537,19 +537,22 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
         dma16_sc1(poll_lds + (gs & 1) * 128, rs, 16u * lane);
       }
     };
-    // copy the partner's scores of `step` into S once all 16 entries carry
-    // the step's tag (the poll has landed); re-poll while they do not
-    auto check = [&](int step) {
+    // copy the partner's scores of `step` into S if all 16 polled entries
+    // carry the step's tag; returns false (S untouched) otherwise
+    auto try_check = [&](int step) -> bool {
       const int gs = gstep + step;
       const uint32_t want = ep | ((uint32_t)gs & 0xffffu);
+      const unsigned long long v = lane < 16 ? pollbuf[wave * 32 + (gs & 1) * 16 + lane] : 0ull;
+      const bool ok = __all(lane >= 16 || (uint32_t)(v >> 32) == want);
+      if (ok && lane < 16)
+        S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float((uint32_t)v);
+      return ok;
+    };
+    // the same, re-polling synchronously until the entries arrive (bounded)
+    auto check = [&](int step) {
+      const int gs = gstep + step;
       uint32_t tries = 0;
-      while (true) {
-        const unsigned long long v = lane < 16 ? pollbuf[wave * 32 + (gs & 1) * 16 + lane] : 0ull;
-        const bool ok = lane >= 16 || (uint32_t)(v >> 32) == want;
-        if (__all(ok)) {
-          if (lane < 16) S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float((uint32_t)v);
-          break;
-        }
+      while (!try_check(step)) {
         if (failed || ++tries > kPollSpinLimit) {
           failed = true;
           if (lane < 16) S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float(kQuietNaN);
@@ -579,30 +582,30 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
     for (int s = 0; s < 8; ++s) acc[s] = f32x16{0};
     const int nsteps = (n + kStepTokens - 1) / kStepTokens;
 
-    // prologue: ring steps 0..3; scores of steps 0..2 published, the
-    // partner's of step 0 in S, its step 1 polled; B operands of step 0;
-    // step 4 in flight.  The queue ends with poll(1), publish(2), step 4.
+    // prologue: ring steps 0..3 landed; the own heads' scores of steps 0..2
+    // published and the partner's of step 0 in S; B operands of step 0;
+    // step 4 in flight.
     s16x4 bcur[8];
 #pragma unroll
     for (int s = 0; s < NST; ++s) issue(s);
     wait_vmcnt<0>();
     publish(0);
     publish(1);
+    publish(2);
     wait_lgkmcnt0();
     poll(0);
     wait_vmcnt<0>();
     check(0);
-    poll(1);
-    publish(2);
     b_operands(0, bcur);
     wait_lgkmcnt0();
     issue(NST);
     barrier();
 
     for (int st = 0; st < nsteps; ++st) {
-      wait_vmcnt<1 + LPS>();  // poll(st+1) and step st+3 have landed
-      check(st + 1);
-      poll(st + 2);
+      // ring step st+3 has landed (the wait for poll(st) at the end of the
+      // previous step covered it); the partner's step st+1 was published two
+      // steps ago
+      poll(st + 1);
       publish(st + 3);
       s16x4 bnext[8];
       b_operands(st + 1, bnext);
@@ -644,6 +647,10 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bcur[s], acc[s], 0, 0, 0);
       }
+      // the partner's scores of step st+1: poll(st+1) has landed once only
+      // publish(st+3) and the 4 ring loads of step st+5 are younger
+      wait_vmcnt<1 + LPS>();
+      check(st + 1);
 #pragma unroll
       for (int s = 0; s < 8; ++s) bcur[s] = bnext[s];
       barrier();
