@@ -435,7 +435,11 @@ template <int NST>
 __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   constexpr int DH = 128;
   constexpr int LPS = 4;            // DMA instructions per step and wave (own unit only)
-  constexpr int SB = 4096;          // ring slot bytes per wave
+  // a ring slot holds the 4 DMA slabs of a step (rows k and 4+k, 1 KB),
+  // each padded by 64 bytes so that the 8 rows a transpose read touches do
+  // not all start on the same LDS bank
+  constexpr int SLAB = 1024 + 64;
+  constexpr int SB = 4 * SLAB;      // ring slot bytes per wave
   constexpr int NS = 4;             // score buffers (steps i .. i+3)
   static_assert(NST == 4, "ring: slots of steps i+1 .. i+4");
   const AttendBf16Params& p = xp.a;
@@ -479,7 +483,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   char* wring = ring + (size_t)wave * NST * SB;
   const uint32_t wring_s = (uint32_t)reinterpret_cast<uintptr_t>(wring);
   const uint4* rd16 = reinterpret_cast<const uint4*>(wring) + lane;
-  const int tr_off = ((lane & 15) >> 2) * 1024 + (lane >> 5) * 512 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  const int tr_off = ((lane & 15) >> 2) * SLAB + (lane >> 5) * 512 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
   // mailbox entries: this wave publishes entry e = 8*(head within unit) + token
   unsigned long long* mine = xp.mbox + ((size_t)(2 * c + cg) * kMboxDepth * 8 + wave) * 16;
   const unsigned long long* theirs = xp.mbox + ((size_t)(2 * c + 1 - cg) * kMboxDepth * 8 + wave) * 16;
@@ -509,7 +513,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
       const i32x4 rs = buffer_desc(reinterpret_cast<const char*>(kbase) + (left ? done : 0u), left);
       const uint32_t dst = wring_s + (step & (NST - 1)) * SB;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dma16(dst + k * 1024, rs, vo + k * row_bytes);
+      for (int k = 0; k < 4; ++k) dma16(dst + k * SLAB, rs, vo + k * row_bytes);
     };
     // own heads' scores of `step` -> S and the mailbox
     auto publish = [&](int step) {
@@ -517,7 +521,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
       const int sl = step & (NST - 1);
       uint4 ko[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ko[k] = rd16[(sl * SB + k * 1024) / 16];
+      for (int k = 0; k < 4; ++k) ko[k] = rd16[(sl * SB + k * SLAB) / 16];
       float v[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[k] = dot8_split(qh, ql, ko[k]);
@@ -526,14 +530,14 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
         S[(gs & (NS - 1)) * 256 + (ocol / DH) * 8 + (pub_e & 7)] = x;
         const unsigned long long ent =
             ((unsigned long long)(ep | ((uint32_t)gs & 0xffffu)) << 32) | __float_as_uint(x);
-        __hip_atomic_store(mine + (size_t)(gs % kMboxDepth) * 8 * 16 + pub_e, ent, __ATOMIC_RELAXED,
+        __hip_atomic_store(mine + (size_t)((uint32_t)gs % kMboxDepth) * 8 * 16 + pub_e, ent, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     };
     auto poll = [&](int step) {  // partner's entries of `step` -> pollbuf[step & 1]
       const int gs = gstep + step;
       if (lane < 8) {
-        const i32x4 rs = buffer_desc(theirs + (size_t)(gs % kMboxDepth) * 8 * 16, 128u);
+        const i32x4 rs = buffer_desc(theirs + (size_t)((uint32_t)gs % kMboxDepth) * 8 * 16, 128u);
         dma16_sc1(poll_lds + (gs & 1) * 128, rs, 16u * lane);
       }
     };
@@ -738,7 +742,7 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   xp.mbox = reinterpret_cast<unsigned long long*>(a.ws + pl.off_mbox);
   xp.tickets = reinterpret_cast<unsigned long long*>(a.ws + pl.off_tickets);
   xp.epoch = next_epoch();
-  const size_t lds = (size_t)pl.nw * NST * 4096 + 4 * 256 * sizeof(float) +
+  const size_t lds = (size_t)pl.nw * NST * 4 * (1024 + 64) + 4 * 256 * sizeof(float) +
                      (size_t)pl.nw * 32 * sizeof(unsigned long long) + (16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_xchg_kernel<NST>;
   static int lds_allowed = 0;
