@@ -72,7 +72,12 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   if (nch > (1 << 20)) return false;
   p->nch = (int)nch;
   p->nslots = p->nch + B - 1;
-  p->npc = (d + proj_rows(dh) - 1) / proj_rows(dh);
+  {
+    const int big = proj_rows(dh, true);
+    const long long grid = (long long)H * ((d + big - 1) / big) * ((B + 7) / 8);
+    p->proj_rows = grid * 2 >= ncu ? big : proj_rows(dh, false);
+  }
+  p->npc = (d + p->proj_rows - 1) / p->proj_rows;
   size_t off = 0;
   p->off_U = off;
   off += align256((size_t)p->nslots * H * d * sizeof(float));

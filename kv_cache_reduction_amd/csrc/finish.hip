@@ -6,8 +6,8 @@
 // Partials (written by the attend phase) are laid out U[h][slot][d] and
 // ml[slot][2][H] (running max in log2 units, normaliser).
 //
-// merge_project  grid (H, ceil(d/R), ceil(B/8)), R = proj_rows(dh) rows of
-//          W_KV per workgroup.  For each of its (up to 8) sequences b the
+// merge_project  grid (H, ceil(d/R), ceil(B/8)), R rows of W_KV per
+//          workgroup (256, or 64 when that grid would be small).  For each of its (up to 8) sequences b the
 //          workgroup first merges the slots s of b over its R rows
 //          (log-sum-exp):
 //            m* = max_s m_s,  l* = sum_s 2^(m_s - m*) l_s,
@@ -26,7 +26,7 @@ namespace slim {
 
 constexpr int kSeqPerProj = 8;  // sequences per workgroup
 
-template <int DH, bool WBF16>
+template <int DH, bool WBF16, int PR>
 __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __restrict__ lengths,
                                                             const float* __restrict__ U,
                                                             const float* __restrict__ ml,
@@ -35,7 +35,6 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
                                                             int T_max, int nch, int nslots) {
   // projection: thread t covers JW output columns (group jq = t % JQ) over the
   // rows of subset t / JQ
-  constexpr int PR = proj_rows(DH);
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;  // column groups per head
   constexpr int JW = DH >= 8 ? 8 : DH;      // columns per group
   constexpr int NRS = 256 / JQ;             // row subsets
@@ -217,9 +216,8 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(const float* __restric
   out[i] = s;
 }
 
-template <int DH, bool WBF16>
+template <int DH, bool WBF16, int PR>
 static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
-  constexpr int PR = proj_rows(DH);
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;
   constexpr int NRS = 256 / JQ;
   constexpr int NSS = 256 / (PR / 4);
@@ -228,7 +226,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
   const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * NSS + (size_t)a.B + 1) * 4;
-  hipLaunchKernelGGL((merge_project_kernel<DH, WBF16>),
+  hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR>),
                      dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), lds, s, a.lengths,
                      U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots);
   hipError_t e = hipGetLastError();
@@ -241,7 +239,12 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
 
 template <int DH>
 static hipError_t launch_w(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
-  return a.w_bf16 ? launch_t<DH, true>(pl, a, s) : launch_t<DH, false>(pl, a, s);
+  constexpr int big = proj_rows(DH, true), small = proj_rows(DH, false);
+  if (pl.proj_rows == big)
+    return a.w_bf16 ? launch_t<DH, true, big>(pl, a, s) : launch_t<DH, false, big>(pl, a, s);
+  if (pl.proj_rows == small)
+    return a.w_bf16 ? launch_t<DH, true, small>(pl, a, s) : launch_t<DH, false, small>(pl, a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_finish(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {

@@ -18,7 +18,8 @@ struct DecodePlan {
   int nw;          // waves per workgroup (MFMA path)
   int nch;         // token chunks
   int nslots;      // partial slots
-  int npc;         // W_KV row blocks of the projection (proj_rows(dh) rows each)
+  int proj_rows;   // W_KV rows per finish workgroup (proj_rows(dh, large or not))
+  int npc;         // W_KV row blocks of the finish (proj_rows rows each)
   size_t off_U;    // [H, nslots, d] float: unnormalised softmax.K rows per chunk
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
@@ -41,9 +42,13 @@ struct DecodeArgs {
 };
 
 // W_KV rows per finish workgroup: a multiple of the projection's row subsets
-// (256 threads / (dh/8) column groups); 256 rows (1 KB of a partial row per
-// slot) measured fastest for the merge, 64 keeps dh = 256 out of spills
-constexpr int proj_rows(int dh) { return dh > 128 ? 64 : 256; }
+// (256 threads / (dh/8) column groups).  The large block (256 rows, 1 KB of
+// a partial row per slot) is fastest when the grid fills the device; the
+// small one (64 rows, or the row-subset count) gives small problems four
+// times the workgroups.  dh = 256 keeps 64 rows to stay out of spills.
+constexpr int proj_rows(int dh, bool large) {
+  return dh > 128 ? 64 : (large ? 256 : (256 / (dh >= 8 ? dh / 8 : 1) > 64 ? 256 / (dh >= 8 ? dh / 8 : 1) : 64));
+}
 constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
 constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)
 
