@@ -36,5 +36,7 @@ from .mha import (  # noqa: F401
     slim_decode_opt2,
     prefill,
     prefill_loop,
+    generate_step,
+    append_rows,
     err_rel,
 )

@@ -226,3 +226,50 @@ def err_rel(o, o_ref) -> float:
     den = np.abs(o_ref).max()
     num = np.abs(o - o_ref).max()
     return float(num / den) if den > 0 else float(num)
+
+
+# ----------------------------------------------------------------------------
+# the whole generation step
+
+def generate_step(x, W_Q, W_K, W_V, K_cache, lengths, H: int, dh: int, scale: float,
+                  cache: str):
+    """One generation step in the order the Slim Attention article gives
+    (section "K-Cache is All You Need", generation phase): first the query of
+    the new token, q = x . W_Q; then its scores against the K rows cached at
+    earlier steps, their softmax and the attention output (here by the plain
+    definition over explicit values, ``mha_decode``); last, the new token's
+    key k = x . W_K is appended to the cache for the next step.
+
+    x [B, d]; W_Q, W_K, W_V [d, d] (float64 values of whatever the device is
+    given); K_cache [B, T, d] in storage dtype; lengths [B].
+    Returns (o [B, H, dh], k_new [B, d] rounded to the cache format as in
+    ``prefill``, lengths_next [B]).  Sequence b's new row goes to row
+    len_b (clamped to [0, T]); a full cache (len_b = T) takes no new row and
+    keeps its length."""
+    x = np.asarray(x, dtype=np.float64)
+    q = x @ np.asarray(W_Q, dtype=np.float64)
+    K = cache_to_f64(np.asarray(K_cache))
+    V = explicit_values(K_cache, W_K, W_V)
+    o = mha_decode(q, K, V, lengths, H, dh, scale)
+    k_new = prefill(x, W_K, cache)
+    T = K.shape[1]
+    lens = np.array([_clamp_len(n, T) for n in lengths], dtype=np.int64)
+    lengths_next = np.where(lens < T, lens + 1, T)
+    return o, k_new, lengths_next
+
+
+def append_rows(K_cache, k_new, lengths):
+    """The cache after a generation step: row len_b of sequence b replaced by
+    k_new[b] where len_b < T (storage dtype kept; bf16 rows are stored as
+    their bit patterns)."""
+    K = np.array(K_cache, copy=True)
+    T = K.shape[1]
+    for b in range(K.shape[0]):
+        n = _clamp_len(lengths[b], T)
+        if n < T:
+            if K.dtype == np.uint16:
+                v = np.asarray(k_new[b], dtype=np.float64).astype(np.float32).view(np.uint32)
+                K[b, n] = (v >> np.uint32(16)).astype(np.uint16)  # exact: already bf16 values
+            else:
+                K[b, n] = k_new[b]
+    return K

@@ -346,3 +346,106 @@ def test_pins_catch_transposed_wkv():
     g = _load("hand_two_heads.json")
     args = (np.array([g["q"]]), np.array([g["K"]]), np.array(g["W_KV"]).T, [2], g["H"], g["dh"], g["scale"])
     assert np.abs(oracle.slim_decode_opt2(*args) - np.array([g["o"]])).max() > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# the generation step: attend over the rows cached at earlier steps, then append
+
+def _step_weights(seed, d):
+    rng = np.random.default_rng(seed)
+    Qo, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    Ro, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    W_K = (Qo * rng.uniform(0.5, 2.0, size=d)[None, :]) @ Ro
+    return rng.standard_normal((d, d)) / math.sqrt(d), W_K, rng.standard_normal((d, d)) / math.sqrt(d)
+
+
+def _causal_excl_loop(X, W_Q, W_K, W_V, H, dh, scale):
+    """Textbook attention of token i over tokens t < i (no self term), pure
+    float64 loops on unrounded K = X W_K and V = X W_V; token 0 gets zeros."""
+    n, d = X.shape
+    Q, K, V = X @ W_Q, X @ W_K, X @ W_V
+    out = np.zeros((n, H, dh))
+    for i in range(1, n):
+        for h in range(H):
+            s = []
+            for t in range(i):
+                s.append(scale * sum(Q[i, h * dh + j] * K[t, h * dh + j] for j in range(dh)))
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            for j in range(dh):
+                out[i, h, j] = sum(e[t] * V[t, h * dh + j] for t in range(i)) / z
+    return out
+
+
+def _run_steps(step_fn, X, W_Q, W_K, W_V, H, dh, T):
+    """Feeds the rows of X one per step into an initially empty float32 cache."""
+    d = X.shape[1]
+    K = np.zeros((1, T, d), dtype=np.float32)
+    lens = np.array([0])
+    outs = []
+    for i in range(X.shape[0]):
+        o, k_new, lens_next = step_fn(X[i:i + 1], W_Q, W_K, W_V, K, lens, H, dh, 1 / math.sqrt(dh), "f32")
+        K = oracle.append_rows(K, k_new, lens)
+        lens = lens_next
+        outs.append(o[0])
+    return np.stack(outs), K, lens
+
+
+def test_step_sequence_is_strictly_causal_attention():
+    H, dh, n = 2, 4, 7
+    d = H * dh
+    W_Q, W_K, W_V = _step_weights(11, d)
+    X = np.random.default_rng(12).standard_normal((n, d))
+    got, K, lens = _run_steps(oracle.generate_step, X, W_Q, W_K, W_V, H, dh, T=n + 2)
+    want = _causal_excl_loop(X, W_Q, W_K, W_V, H, dh, 1 / math.sqrt(dh))
+    assert np.abs(got[0]).max() == 0                       # nothing cached yet
+    assert _rel(got, want) < 1e-5                          # float32 cache rounding only
+    assert int(lens[0]) == n
+    assert np.abs(K[0, :n] - (X @ W_K)).max() < 1e-5 * np.abs(X @ W_K).max()
+    assert np.all(K[0, n:] == 0)
+
+
+def test_step_full_and_bf16_cache():
+    H, dh, T = 2, 4, 5
+    d = H * dh
+    W_Q, W_K, W_V = _step_weights(13, d)
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((3, T, d))
+    K = np.stack([syn.f32_to_bf16_bits((X[b] @ W_K).astype(np.float32)) for b in range(3)])
+    lens = np.array([T, 2, 0])
+    x = rng.standard_normal((3, d))
+    o, k_new, nxt = oracle.generate_step(x, W_Q, W_K, W_V, K, lens, H, dh, 0.5, "bf16")
+    assert list(nxt) == [T, 3, 1]
+    assert np.abs(o[2]).max() == 0
+    assert np.abs(k_new - oracle.round_bf16(x @ W_K)).max() == 0
+    K2 = oracle.append_rows(K, k_new, lens)
+    assert np.array_equal(K2[0], K[0])                       # full: untouched
+    assert np.array_equal(oracle.bf16_decode(K2[1, 2]), k_new[1])
+    assert np.array_equal(oracle.bf16_decode(K2[2, 0]), k_new[2])
+    assert np.array_equal(np.delete(K2[1], 2, axis=0), np.delete(K[1], 2, axis=0))
+
+
+def _mut_step_append_first(x, W_Q, W_K, W_V, K_cache, lengths, H, dh, scale, cache):
+    k_new = oracle.prefill(x, W_K, cache)
+    K2 = oracle.append_rows(K_cache, k_new, lengths)
+    T = K2.shape[1]
+    lens = np.minimum(np.asarray(lengths) + 1, T)
+    q = np.asarray(x, dtype=np.float64) @ W_Q
+    o = oracle.mha_decode(q, oracle.cache_to_f64(K2), oracle.explicit_values(K2, W_K, W_V), lens, H, dh, scale)
+    return o, k_new, lens
+
+
+def _mut_step_query_from_wk(x, W_Q, W_K, W_V, K_cache, lengths, H, dh, scale, cache):
+    return oracle.generate_step(x, W_K, W_K, W_V, K_cache, lengths, H, dh, scale, cache)
+
+
+@pytest.mark.parametrize("mutant", [_mut_step_append_first, _mut_step_query_from_wk])
+def test_step_pin_catches_planted_mistakes(mutant):
+    H, dh, n = 2, 4, 6
+    d = H * dh
+    W_Q, W_K, W_V = _step_weights(15, d)
+    X = np.random.default_rng(16).standard_normal((n, d))
+    want = _causal_excl_loop(X, W_Q, W_K, W_V, H, dh, 1 / math.sqrt(dh))
+    got, _, _ = _run_steps(mutant, X, W_Q, W_K, W_V, H, dh, T=n + 1)
+    assert _rel(got, want) > 1e-3
