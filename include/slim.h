@@ -164,6 +164,46 @@ slim_status_t slim_decode_finish(const float* q,
                                  hipStream_t stream);
 
 /*
+ * slim_step -- one whole generation step for B sequences, in the order of the
+ * Slim Attention article (section "K-Cache is All You Need", generation
+ * phase): the new token's query, its attention over the K rows cached at
+ * earlier steps with V recovered through W_KV (as slim_decode), and at the
+ * end the new token's key appended to the cache for the next step.
+ *   x        : device float32 [B, d], the new tokens' inputs
+ *   W_Q, W_K : device [d, d] in w_dt (f32 or bf16): q = x.W_Q, k = x.W_K,
+ *              both accumulated in float32
+ *   K_cache  : device [B, T_max, d] in k_dt, read AND written: sequence b
+ *              attends over rows [0, len_b), then row len_b receives
+ *              round(k_b) (round to nearest even for bf16) when len_b < T_max;
+ *              a full cache (len_b = T_max) takes no new row.  No other row
+ *              is written.
+ *   lengths  : device int32 [B], len_b before the step, clamped to [0, T_max]
+ *   lengths_next : device int32 [B], written: len_b + 1, or T_max for a full
+ *              cache.  Must not overlap `lengths` (callers alternate two
+ *              buffers from step to step).
+ *   W_KV, wkv_dt, out, scale : as slim_decode (out[b] is the attention output
+ *              of the new token of sequence b; q itself stays in the workspace)
+ *   workspace : at least slim_step_workspace_bytes(B, H, dh, T_max, k_dt)
+ *              bytes, 16-byte aligned.
+ * Kernels, in stream order: the q/k projection (reduction split over row
+ * blocks of W), its sum (writes q to the workspace, k to the cache,
+ * lengths_next), then the decode kernels.  Shape support as slim_decode, and
+ * d % 8 == 0.  Alignment: W_Q, W_K 16 bytes; x, lengths_next 4 bytes.
+ * Errors: as slim_decode; SLIM_ERR_INVALID also for null x/W_Q/W_K/
+ * lengths_next or lengths_next == lengths.
+ */
+size_t slim_step_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t k_dt);
+slim_status_t slim_step(const float* x,
+                        const void* W_Q, const void* W_K, slim_dtype_t w_dt,
+                        void* K_cache, slim_dtype_t k_dt,
+                        const int32_t* lengths, int32_t* lengths_next,
+                        const void* W_KV, slim_dtype_t wkv_dt,
+                        float* out,
+                        int B, int H, int dh, int T_max, float scale,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * mha_decode_kv -- comparator: standard MHA decode over explicit K and V
  * caches (the baseline the Slim Attention article halves), same conventions
  * as slim_decode with V_cache [B, T_max, d] in kv_dt in place of W_KV:

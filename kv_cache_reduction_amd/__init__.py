@@ -5,7 +5,7 @@ kernels of libslim.so, which this module loads with ctypes.  torch tensors
 supply device memory and the current HIP stream.  There is no fallback: if
 the library is missing, importing this package raises ImportError.
 
-Build it with ``python -m kv_cache_reduction_amd.build`` (or
+Build it with ``python kv_cache_reduction_amd/build.py`` (or
 ``__graft_entry__.build()``).
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libslim.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m kv_cache_reduction_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python kv_cache_reduction_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -42,6 +42,11 @@ for _name in ("slim_decode", "slim_decode_attend", "slim_decode_finish"):
     _fn = getattr(lib, _name)
     _fn.restype = _i
     _fn.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+lib.slim_step_workspace_bytes.restype = _sz
+lib.slim_step_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+lib.slim_step.restype = _i
+lib.slim_step.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _sz,
+                          _vp]
 lib.mha_decode_kv_workspace_bytes.restype = _sz
 lib.mha_decode_kv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mha_decode_kv.restype = _i
@@ -172,6 +177,32 @@ def decode_attend(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, st
 def decode_finish(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, stream=None) -> None:
     _check(lib.slim_decode_finish(*_decode_args(q, K_cache, lengths, W_KV, out, H, dh, scale, ws),
                                   _stream(stream)), "slim_decode_finish")
+
+
+def step_workspace_bytes(B: int, H: int, dh: int, T_max: int, k_dtype) -> int:
+    code = k_dtype if isinstance(k_dtype, int) else _dt_of(k_dtype)
+    return int(lib.slim_step_workspace_bytes(B, H, dh, T_max, code))
+
+
+def step(x, W_Q, W_K, K_cache, lengths, lengths_next, W_KV, out, H, dh, scale=None, ws=None,
+         stream=None) -> None:
+    """One whole generation step (see slim_step in include/slim.h): q and k
+    from x, attention over the cached rows, then k appended at row len_b and
+    lengths_next written."""
+    B, T_max, d = K_cache.shape
+    if x.shape != (B, d) or W_Q.shape != (d, d) or W_K.shape != (d, d) or W_Q.dtype != W_K.dtype:
+        raise ValueError("shape mismatch")
+    if lengths_next.shape != (B,):
+        raise ValueError("shape mismatch")
+    torch = _torch()
+    if x.dtype != torch.float32 or lengths_next.dtype != torch.int32:
+        raise TypeError("x is float32, lengths int32")
+    if ws is None:
+        ws = workspace(step_workspace_bytes(B, H, dh, T_max, K_cache.dtype), x.device)
+    a = _decode_args(x, K_cache, lengths, W_KV, out, H, dh, scale, ws)
+    _check(lib.slim_step(_dev(x), _dev(W_Q), _dev(W_K), _dt(W_Q), _dev(K_cache), _dt(K_cache),
+                         _dev(lengths), _dev(lengths_next), _dev(W_KV), _dt(W_KV), _dev(out),
+                         B, H, dh, T_max, a[11], _dev(ws), ws.numel(), _stream(stream)), "slim_step")
 
 
 def mha_kv_workspace_bytes(B: int, H: int, dh: int, T_max: int, dtype) -> int:

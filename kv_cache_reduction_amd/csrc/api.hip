@@ -9,6 +9,7 @@
 
 #include "slim.h"
 #include "internal.hpp"
+#include "step.hpp"
 
 namespace slim {
 
@@ -179,10 +180,11 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
 
 enum DecodeMode { kFull = 0, kAttend = 1, kFinish = 2 };
 
-static slim_status_t decode_common(int mode, const float* q, const void* K_cache, slim_dtype_t k_dt,
-                                   const int32_t* lengths, const void* W_KV, slim_dtype_t w_dt,
-                                   float* out, int B, int H, int dh, int T_max, float scale,
-                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Host checks and plan of a decode call, everything but the workspace size.
+static slim_status_t decode_prepare(const float* q, const void* K_cache, slim_dtype_t k_dt,
+                                    const int32_t* lengths, const void* W_KV, slim_dtype_t w_dt,
+                                    float* out, int B, int H, int dh, int T_max, float scale,
+                                    void* workspace, DecodePlan* plan, DecodeArgs* a) {
   if (!q || !K_cache || !lengths || !W_KV || !out || !workspace) return SLIM_ERR_INVALID;
   if (!std::isfinite(scale)) return SLIM_ERR_INVALID;
   slim_status_t st = decode_shape_ok(B, H, dh, T_max, k_dt);
@@ -193,29 +195,43 @@ static slim_status_t decode_common(int mode, const float* q, const void* K_cache
     return SLIM_ERR_INVALID;
   int ncu = 0;
   if (device_cus(&ncu) != 0) return SLIM_ERR_HIP;
-  DecodePlan plan;
-  if (!make_decode_plan(B, H, dh, T_max, k_dt == SLIM_BF16, ncu, &plan)) return SLIM_ERR_UNSUPPORTED;
-  if (workspace_bytes < plan.bytes) return SLIM_ERR_WORKSPACE;
-  DecodeArgs a;
-  a.q = q;
-  a.K = K_cache;
-  a.lengths = lengths;
-  a.W = W_KV;
-  a.out = out;
-  a.B = B;
-  a.H = H;
-  a.dh = dh;
-  a.d = H * dh;
-  a.T_max = T_max;
-  a.nslots = plan.nslots;
-  a.scale = scale;
-  a.w_bf16 = w_dt == SLIM_BF16;
-  a.ws = static_cast<char*>(workspace);
+  if (!make_decode_plan(B, H, dh, T_max, k_dt == SLIM_BF16, ncu, plan)) return SLIM_ERR_UNSUPPORTED;
+  a->q = q;
+  a->K = K_cache;
+  a->lengths = lengths;
+  a->W = W_KV;
+  a->out = out;
+  a->B = B;
+  a->H = H;
+  a->dh = dh;
+  a->d = H * dh;
+  a->T_max = T_max;
+  a->nslots = plan->nslots;
+  a->scale = scale;
+  a->w_bf16 = w_dt == SLIM_BF16;
+  a->ws = static_cast<char*>(workspace);
+  return SLIM_OK;
+}
+
+static hipError_t decode_launch(int mode, const DecodePlan& plan, const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (mode == kFull || mode == kAttend)
     e = plan.bf16_k ? launch_attend_bf16(plan, a, stream) : launch_attend_f32(plan, a, stream);
   if (e == hipSuccess && (mode == kFull || mode == kFinish)) e = launch_finish(plan, a, stream);
-  return e == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+  return e;
+}
+
+static slim_status_t decode_common(int mode, const float* q, const void* K_cache, slim_dtype_t k_dt,
+                                   const int32_t* lengths, const void* W_KV, slim_dtype_t w_dt,
+                                   float* out, int B, int H, int dh, int T_max, float scale,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  DecodePlan plan;
+  DecodeArgs a;
+  slim_status_t st = decode_prepare(q, K_cache, k_dt, lengths, W_KV, w_dt, out, B, H, dh, T_max, scale,
+                                    workspace, &plan, &a);
+  if (st != SLIM_OK) return st;
+  if (workspace_bytes < plan.bytes) return SLIM_ERR_WORKSPACE;
+  return decode_launch(mode, plan, a, stream) == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 slim_status_t slim_decode(const float* q, const void* K_cache, slim_dtype_t k_dt,
@@ -240,6 +256,47 @@ slim_status_t slim_decode_finish(const float* q, const void* K_cache, slim_dtype
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(kFinish, q, K_cache, k_dt, lengths, W_KV, w_dt, out, B, H, dh, T_max, scale,
                        workspace, workspace_bytes, stream);
+}
+
+size_t slim_step_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t k_dt) {
+  if (decode_shape_ok(B, H, dh, T_max, k_dt) != SLIM_OK || (H * dh) % 8 != 0) return 0;
+  int ncu = 0;
+  if (device_cus(&ncu) != 0) return 0;
+  DecodePlan p;
+  StepPlan sp;
+  if (!make_decode_plan(B, H, dh, T_max, k_dt == SLIM_BF16, ncu, &p)) return 0;
+  if (!make_step_plan(B, H * dh, ncu, p.bytes, &sp)) return 0;
+  return sp.bytes;
+}
+
+slim_status_t slim_step(const float* x, const void* W_Q, const void* W_K, slim_dtype_t w_dt,
+                        void* K_cache, slim_dtype_t k_dt, const int32_t* lengths, int32_t* lengths_next,
+                        const void* W_KV, slim_dtype_t wkv_dt, float* out, int B, int H, int dh,
+                        int T_max, float scale, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!x || !W_Q || !W_K || !lengths_next) return SLIM_ERR_INVALID;
+  if (w_dt != SLIM_F32 && w_dt != SLIM_BF16) return SLIM_ERR_UNSUPPORTED;
+  if (((uintptr_t)x & 3u) || !aligned16(W_Q) || !aligned16(W_K) || ((uintptr_t)lengths_next & 3u))
+    return SLIM_ERR_INVALID;
+  if (lengths_next == lengths) return SLIM_ERR_INVALID;
+  if ((long long)H * dh % 8 != 0) return SLIM_ERR_UNSUPPORTED;
+  DecodePlan plan;
+  DecodeArgs a;
+  // q is filled in below; any aligned non-null pointer passes the checks here
+  slim_status_t st = decode_prepare(x, K_cache, k_dt, lengths, W_KV, wkv_dt, out, B, H, dh, T_max, scale,
+                                    workspace, &plan, &a);
+  if (st != SLIM_OK) return st;
+  int ncu = 0;
+  if (device_cus(&ncu) != 0) return SLIM_ERR_HIP;
+  StepPlan sp;
+  if (!make_step_plan(B, H * dh, ncu, plan.bytes, &sp)) return SLIM_ERR_UNSUPPORTED;
+  if (workspace_bytes < sp.bytes) return SLIM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = launch_step_qk(sp, x, W_Q, W_K, w_dt == SLIM_BF16, K_cache, k_dt == SLIM_BF16, lengths,
+                                lengths_next, B, H * dh, T_max, ws, stream);
+  if (e != hipSuccess) return SLIM_ERR_HIP;
+  a.q = reinterpret_cast<const float*>(ws + sp.off_q);
+  return decode_launch(kFull, plan, a, stream) == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 static slim_status_t kv_shape_ok(int B, int H, int dh, int T_max, slim_dtype_t kv_dt) {

@@ -1,0 +1,199 @@
+"""GPU parity of the whole generation step (slim_step through the C ABI):
+q = x.W_Q and k = x.W_K on the device, attention over the rows cached at
+earlier steps, then k appended at row len_b.  Against the float64 oracle's
+generate_step on the same seeded inputs: the attention output to the decode
+tolerance, the appended row to one bf16 ulp (plus the float32 summation
+bound), lengths_next exactly, and every other cache row bit-identical."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from gpu_common import TOL, bf16_bits, check_prefill_bf16, log, oracle_decode, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights_dev(cfg, w):
+    """The step's W_Q and W_K as stored on the device (float32, or bf16 for
+    bf16 caches), their float64 values, and W_KV from that same W_K."""
+    import kv_cache_reduction_amd as slim
+    if cfg.cache == "bf16":
+        WQb = syn.f32_to_bf16_bits(w.W_Q.astype(np.float32))
+        WKb = syn.f32_to_bf16_bits(w.W_K.astype(np.float32))
+        WQ64, WK64 = oracle.bf16_decode(WQb), oracle.bf16_decode(WKb)
+        WQd, WKd = to_dev(WQb), to_dev(WKb)
+    else:
+        WQ32, WK32 = w.W_Q.astype(np.float32), w.W_K.astype(np.float32)
+        WQ64, WK64 = WQ32.astype(np.float64), WK32.astype(np.float64)
+        WQd, WKd = to_dev(WQ32), to_dev(WK32)
+    Wkv = to_dev(slim.wkv(WK64, w.W_V, cfg.wkv))
+    return WQd, WKd, WQ64, WK64, Wkv
+
+
+def _gpu_step(cfg, x, WQd, WKd, Kd, lens, Wkv, ws=None):
+    import torch
+    import kv_cache_reduction_amd as slim
+    B = x.shape[0]
+    out = torch.empty((B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+    ld = to_dev(np.asarray(lens, dtype=np.int32))
+    nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    slim.step(to_dev(x.astype(np.float32)), WQd, WKd, Kd, ld, nxt, Wkv, out, cfg.H, cfg.dh, cfg.scale, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), nxt.cpu().numpy()
+
+
+def _cache_np(Kd, cfg):
+    return bf16_bits(Kd) if cfg.cache == "bf16" else Kd.cpu().numpy()
+
+
+def _check_rows(name, cfg, K_before, K_after, lens, x, WK64):
+    """Appended rows against the float64 product; all other rows untouched."""
+    B, T = K_before.shape[:2]
+    rows = [(b, int(min(max(lens[b], 0), T))) for b in range(B)]
+    app = [(b, t) for b, t in rows if t < T]
+    mask = np.ones((B, T), dtype=bool)
+    for b, t in app:
+        mask[b, t] = False
+    assert np.array_equal(K_after[mask], K_before[mask]), f"{name}: rows other than len_b changed"
+    if not app:
+        return
+    bs = [b for b, _ in app]
+    got = np.stack([K_after[b, t] for b, t in app])
+    X = x[bs].astype(np.float64)
+    if cfg.cache == "bf16":
+        check_prefill_bf16(got, X, WK64, f"{name} appended rows")
+    else:
+        ref = X @ WK64
+        bound = 4 * X.shape[1] * 2.0 ** -24 * (np.abs(X) @ np.abs(WK64)) + 2.0 ** -24 * np.abs(ref)
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= bound)
+
+
+def _run_case(name, cfg, lens, T_alloc=None, seed_shift=0):
+    import torch
+    w = syn.weights(cfg)
+    lens = np.asarray(lens, dtype=np.int32)
+    T_alloc = cfg.T_max if T_alloc is None else T_alloc
+    K = syn.k_cache(cfg, w, np.minimum(lens, T_alloc), T_alloc=T_alloc)
+    x = syn.x_new(cfg) if seed_shift == 0 else np.random.default_rng(seed_shift).standard_normal(
+        (cfg.B, cfg.d)).astype(np.float32)
+    WQd, WKd, WQ64, WK64, Wkv = _weights_dev(cfg, w)
+    Kd = to_dev(K)
+    log(f"[step] {name}: B={cfg.B} d={cfg.d} H={cfg.H} dh={cfg.dh} T={T_alloc} lens={lens.tolist()}")
+    o, nxt = _gpu_step(cfg, x, WQd, WKd, Kd, lens, Wkv)
+    o_ref, k_ref, nxt_ref = oracle.generate_step(x.astype(np.float64), WQ64, WK64, w.W_V, K, lens,
+                                                 cfg.H, cfg.dh, cfg.scale, cfg.cache)
+    err = oracle.err_rel(o, o_ref)
+    log(f"[step] {name}: err={err:.3e} lengths_next={nxt.tolist()}")
+    assert np.isfinite(o).all()
+    assert err <= TOL[cfg.cache]
+    assert np.array_equal(nxt, nxt_ref)
+    _check_rows(name, cfg, K, _cache_np(Kd, cfg), lens, x, WK64)
+    return o
+
+
+def test_step_c0_fp32():
+    cfg = syn.CONFIGS["c0"]
+    _run_case("c0", cfg, [20])
+
+
+def test_step_c0_fp32_full_and_empty():
+    cfg = syn.shrink(syn.CONFIGS["c0"], B=3, T_max=32)
+    _run_case("c0 full/empty", cfg, [32, 0, 31])
+
+
+def test_step_c1_shape_ragged():
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=6, T_max=200, len_lo=0, len_hi=200)
+    _run_case("c1-shaped", cfg, [0, 1, 200, 77, 150, 199])
+
+
+def test_step_c2_shape_two_column_groups():
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=3, T_max=300, len_lo=0, len_hi=300)
+    _run_case("c2-shaped", cfg, [300, 129, 0])
+
+
+def test_step_c4_shape_two_sequence_groups():
+    # B = 20: the projection handles 16 sequences per workgroup, so two groups
+    cfg = syn.shrink(syn.CONFIGS["c4"], B=20, T_max=64, len_lo=0, len_hi=64)
+    lens = (np.arange(20) * 7) % 65
+    _run_case("c4-shaped", cfg, lens)
+
+
+def test_step_two_steps_alternating_lengths():
+    import torch
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=3, T_max=96, len_lo=0, len_hi=96)
+    w = syn.weights(cfg)
+    lens0 = np.array([5, 95, 0], dtype=np.int32)
+    K = syn.k_cache(cfg, w, lens0)
+    WQd, WKd, WQ64, WK64, Wkv = _weights_dev(cfg, w)
+    rng = np.random.default_rng(77)
+    xs = rng.standard_normal((2, cfg.B, cfg.d)).astype(np.float32)
+    Kd = to_dev(K)
+    la, lb = to_dev(lens0), torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    outs = []
+    ws = slim.workspace(slim.step_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, Kd.dtype))
+    for i in range(2):
+        out = torch.empty((cfg.B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+        slim.step(to_dev(xs[i]), WQd, WKd, Kd, la, lb, Wkv, out, cfg.H, cfg.dh, cfg.scale, ws)
+        outs.append(out)
+        la, lb = lb, la
+    torch.cuda.synchronize()
+    Kr, lr = K, lens0
+    for i in range(2):
+        o_ref, k_ref, nxt = oracle.generate_step(xs[i].astype(np.float64), WQ64, WK64, w.W_V, Kr, lr,
+                                                 cfg.H, cfg.dh, cfg.scale, cfg.cache)
+        err = oracle.err_rel(outs[i].cpu().numpy(), o_ref)
+        log(f"[step] two steps, step {i}: err={err:.3e}")
+        assert err <= TOL["bf16"]
+        Kr = oracle.append_rows(Kr, k_ref, lr)
+        lr = nxt
+    assert np.array_equal(la.cpu().numpy(), lr)        # after two swaps la holds the last lengths
+    assert np.array_equal(lr, [7, 96, 2])
+    got = bf16_bits(Kd)
+    # rows written by the device vs the oracle's rounding: at most one bf16 ulp apart
+    diff = np.abs(oracle.bf16_decode(got) - oracle.bf16_decode(Kr))
+    mag = np.maximum(np.abs(oracle.bf16_decode(Kr)), 2.0 ** -126)
+    assert np.all(diff <= 2.0 ** (np.floor(np.log2(mag)) - 7) * 1.0001)
+
+
+def test_step_rejects_aliased_lengths():
+    import torch
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=2, T_max=16)
+    w = syn.weights(cfg)
+    WQd, WKd, _, _, Wkv = _weights_dev(cfg, w)
+    Kd = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
+    ld = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+    x = torch.zeros((cfg.B, cfg.d), dtype=torch.float32, device="cuda")
+    with pytest.raises(slim.SlimError):
+        slim.step(x, WQd, WKd, Kd, ld, ld, Wkv, out, cfg.H, cfg.dh, cfg.scale)
+
+
+def test_step_c3_full_size_sampled_heads():
+    """The long-context step at its real size: 131071 cached rows of d=4096,
+    the new row lands at 131071.  Sampled heads against the oracle, the
+    appended row in full."""
+    cfg = syn.CONFIGS["c3"]
+    w = syn.weights(cfg)
+    T = cfg.T_max
+    lens = np.array([T - 1], dtype=np.int32)
+    log(f"[step] c3 full size: generating {T - 1} rows")
+    K = syn.k_cache(cfg, w, lens)
+    x = syn.x_new(cfg)
+    WQd, WKd, WQ64, WK64, Wkv = _weights_dev(cfg, w)
+    Kd = to_dev(K)
+    o, nxt = _gpu_step(cfg, x, WQd, WKd, Kd, lens, Wkv)
+    assert np.isfinite(o).all()
+    assert nxt.tolist() == [T]
+    q = x.astype(np.float64) @ WQ64
+    heads = [0, 21, 31]
+    ref = oracle_decode(cfg, q, K, lens, WK64, w.W_V, heads=heads, reassociate=True)
+    err = oracle.err_rel(o[:, heads], ref)
+    log(f"[step] c3 full size: err={err:.3e}")
+    assert err <= TOL["bf16"]
+    got = bf16_bits(Kd[:, T - 1])
+    check_prefill_bf16(got, x.astype(np.float64), WK64, "c3 appended row")
