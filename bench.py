@@ -84,6 +84,7 @@ class Workload:
         # the device K cache is built from bf16 W_K, so W_KV comes from the same matrix
         WK = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))).astype(np.float64)
         self.lens = syn.lengths(cfg)
+        self.w, self.WK = w, WK
         self.q = torch.from_numpy(syn.queries(cfg, w)).cuda()
         self.ld = torch.from_numpy(self.lens).cuda()
         log(f"[bench] {name}: weights {time.time() - t:.1f}s")
@@ -127,6 +128,32 @@ def time_slim(wl, torch, slim, steps, warmup):
     ms_step = start.elapsed_time(stop) / steps
     attend = np.array([a0[i].elapsed_time(a1[i]) for i in range(steps)])
     return ms_step, attend
+
+
+def time_step(wl, torch, slim, steps, warmup):
+    """The whole generation step (slim_step): q and k from the new token's x
+    by bf16 W_Q and W_K, attention over len_b - 1 cached rows, k appended at
+    row len_b - 1 (the same row every step, so the cache never fills)."""
+    import synthetic as syn
+    cfg = wl.cfg
+    WQ = bf16_dev(syn.f32_to_bf16_bits(wl.w.W_Q.astype(np.float32)))
+    WK = bf16_dev(syn.f32_to_bf16_bits(wl.WK.astype(np.float32)))
+    x = torch.from_numpy(syn.x_new(cfg)).cuda()
+    lens = torch.from_numpy(np.maximum(wl.lens - 1, 0).astype(np.int32)).cuda()
+    nxt = torch.empty_like(lens)
+    ws = slim.workspace(slim.step_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, slim.BF16))
+    args = lambda i: (x, WQ, WK, wl.K[i % len(wl.K)], lens, nxt, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, ws)
+    for i in range(warmup):
+        slim.step(*args(i))
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        slim.step(*args(i))
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
 
 
 def time_kv(wl, torch, slim, steps, warmup):
@@ -306,6 +333,16 @@ def main():
     }
 
     if not args.no_extras:
+        ms_gen = time_step(wl, torch, slim, max(10, args.steps // 2), 3)
+        wbytes = 2 * cfg.d * cfg.d * 2
+        res["generation_step"] = {
+            "what": ("slim_step: q = x.W_Q and k = x.W_K (bf16 weights, fp32 accumulate), attention "
+                     "over len_b - 1 cached rows, k appended at row len_b - 1"),
+            "tokens_s": cfg.B / (ms_gen * 1e-3), "ms_per_step": ms_gen,
+            "over_decode_us": (ms_gen - ms_step) * 1e3,
+            "projection_weight_bytes": wbytes}
+        log(f"[bench] generation step: {ms_gen * 1e3:.1f} us/step "
+            f"({(ms_gen - ms_step) * 1e3:.1f} us over the decode)")
         ms_kv = time_kv(wl, torch, slim, max(10, args.steps // 2), 3)
         res["comparator"] = {"what": "standard MHA decode over explicit bf16 K and V caches (same box)",
                              "tokens_s": cfg.B / (ms_kv * 1e-3), "ms_per_step": ms_kv,

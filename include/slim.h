@@ -184,7 +184,7 @@ slim_status_t slim_decode_finish(const float* q,
  *   W_KV, wkv_dt, out, scale : as slim_decode (out[b] is the attention output
  *              of the new token of sequence b; q itself stays in the workspace)
  *   workspace : at least slim_step_workspace_bytes(B, H, dh, T_max, k_dt)
- *              bytes, 16-byte aligned.
+ *              bytes (enough for either w_dt), 16-byte aligned.
  * Kernels, in stream order: the q/k projection (reduction split over row
  * blocks of W), its sum (writes q to the workspace, k to the cache,
  * lengths_next), then the decode kernels.  Shape support as slim_decode, and

@@ -263,10 +263,12 @@ size_t slim_step_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t k
   int ncu = 0;
   if (device_cus(&ncu) != 0) return 0;
   DecodePlan p;
-  StepPlan sp;
+  StepPlan sp, sp2;
   if (!make_decode_plan(B, H, dh, T_max, k_dt == SLIM_BF16, ncu, &p)) return 0;
-  if (!make_step_plan(B, H * dh, ncu, p.bytes, &sp)) return 0;
-  return sp.bytes;
+  if (!make_step_plan(B, H * dh, ncu, true, p.bytes, &sp) ||
+      !make_step_plan(B, H * dh, ncu, false, p.bytes, &sp2))
+    return 0;
+  return sp.bytes > sp2.bytes ? sp.bytes : sp2.bytes;  // either weight dtype
 }
 
 slim_status_t slim_step(const float* x, const void* W_Q, const void* W_K, slim_dtype_t w_dt,
@@ -289,7 +291,7 @@ slim_status_t slim_step(const float* x, const void* W_Q, const void* W_K, slim_d
   int ncu = 0;
   if (device_cus(&ncu) != 0) return SLIM_ERR_HIP;
   StepPlan sp;
-  if (!make_step_plan(B, H * dh, ncu, plan.bytes, &sp)) return SLIM_ERR_UNSUPPORTED;
+  if (!make_step_plan(B, H * dh, ncu, w_dt == SLIM_BF16, plan.bytes, &sp)) return SLIM_ERR_UNSUPPORTED;
   if (workspace_bytes < sp.bytes) return SLIM_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipError_t e = launch_step_qk(sp, x, W_Q, W_K, w_dt == SLIM_BF16, K_cache, k_dt == SLIM_BF16, lengths,

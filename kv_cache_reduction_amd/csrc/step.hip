@@ -11,7 +11,8 @@
 //           grid (ceil(2d/512), ks, ceil(B/BG)), 512 threads.  A workgroup
 //           owns 512 output columns (8 per lane, one 16-byte row segment of
 //           bf16 W per load) and KR rows of W; its 8 waves take every 8th row
-//           and meet in LDS at the end.  x[b, rows] for BG sequences sits in
+//           in batches of 8 (4 for float32 W), two batches in flight, and
+//           meet in LDS at the end.  x[b, rows] for BG sequences sits in
 //           LDS, read as broadcasts.  W is read once per BG sequences.
 //           part[ks][B][2d] float.
 // qk_finish sums the ks partials of every output in a fixed order; q goes to
@@ -26,28 +27,74 @@ namespace slim {
 constexpr int kQkCols = 512;  // output columns per workgroup (64 lanes x 8)
 constexpr int kQkWaves = 8;
 
-template <bool WBF16, int BG>
+// Rows of W per batch and lane (the raw row segments, 4 registers per row
+// for bf16 and 8 for float32, take 32 registers per batch; two batches are
+// in flight next to the BG x 8 accumulators).
+template <bool WBF16>
+constexpr int qk_batch_rows() {
+  return WBF16 ? 8 : 4;
+}
+// rows of W per workgroup: 8 waves x U rows x NB batches
+template <bool WBF16, int NB>
+constexpr int qk_block_rows() {
+  return kQkWaves * qk_batch_rows<WBF16>() * NB;
+}
+
+// Straight-line code (NB batches unrolled, every load unconditional with
+// its row clamped into the block) so that the compiler's wait counts let a
+// batch arrive while the previous one is summed.
+template <bool WBF16, int BG, int NB>
 __global__ void __launch_bounds__(512) qk_proj_kernel(const float* __restrict__ x,
                                                       const void* __restrict__ WQ,
                                                       const void* __restrict__ WK,
-                                                      float* __restrict__ part, int B, int d, int KR) {
+                                                      float* __restrict__ part, int B, int d) {
   extern __shared__ __attribute__((aligned(16))) float qk_smem[];
   constexpr int CB = BG < 4 ? BG : 4;  // sequences per round of the cross-wave sum
+  constexpr int U = qk_batch_rows<WBF16>();
+  constexpr int KR = qk_block_rows<WBF16, NB>();
+  constexpr int RW = WBF16 ? 1 : 2;    // 16-byte loads per row segment
+  constexpr int XPT = (KR * BG + 511) / 512;  // x values staged per thread
+  constexpr int esz = WBF16 ? 2 : 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.y * KR, nk = min(KR, d - k0);
   const int b0 = blockIdx.z * BG;
 
-  float* xs = qk_smem;  // [KR][BG]
-  for (int i = tid; i < nk * BG; i += 512) {
-    const int k = i / BG, bb = i - k * BG;
-    xs[i] = b0 + bb < B ? x[(size_t)(b0 + bb) * d + k0 + k] : 0.f;
+  // x[b0 + bb, k0 + k] for the block, loads first (indexes clamped; the
+  // values outside are replaced by zero when stored)
+  float xv_st[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int i = tid + 512 * j, k = i / BG, bb = i - k * BG;
+    const int kk = min(k, nk - 1), b = min(b0 + bb, B - 1);
+    xv_st[j] = x[(size_t)b * d + k0 + kk];
   }
-  __syncthreads();
 
   const int col = blockIdx.x * kQkCols + lane * 8;  // column of [q | k]
   const bool live = col < 2 * d;
-  const int wc = col < d ? col : col - d;
-  const void* W = col < d ? WQ : WK;
+  const int cl = live ? col : 0;
+  const int wc = cl < d ? cl : cl - d;
+  const char* W = static_cast<const char*>(cl < d ? WQ : WK);
+
+  uint4 buf[2][U][RW];
+  auto load = [&](uint4 (&raw)[U][RW], int nb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = min(wave + kQkWaves * (nb * U + u), nk - 1);
+#pragma unroll
+      for (int v = 0; v < RW; ++v)
+        raw[u][v] = *reinterpret_cast<const uint4*>(W + ((size_t)(k0 + r) * d + wc) * esz + 16 * v);
+    }
+  };
+  load(buf[0], 0);
+  if constexpr (NB > 1) load(buf[1], 1);
+
+  float* xs = qk_smem;  // [KR][BG], padded to XPT * 512 so every thread stores
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int i = tid + 512 * j, k = i / BG, bb = i - k * BG;
+    xs[i] = (k < nk && b0 + bb < B) ? xv_st[j] : 0.f;
+  }
+  __syncthreads();
 
   float acc[BG][8];
 #pragma unroll
@@ -55,52 +102,42 @@ __global__ void __launch_bounds__(512) qk_proj_kernel(const float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
-  auto load_row = [&](int k, float (&w)[8]) {
-    const size_t off = (size_t)(k0 + k) * d + wc;
-    if constexpr (WBF16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + off);
-      w[0] = bf_lo(v.x); w[1] = bf_hi(v.x); w[2] = bf_lo(v.y); w[3] = bf_hi(v.y);
-      w[4] = bf_lo(v.z); w[5] = bf_hi(v.z); w[6] = bf_lo(v.w); w[7] = bf_hi(v.w);
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + off);
-      const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + off + 4);
-      w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-      w[4] = c.x; w[5] = c.y; w[6] = c.z; w[7] = c.w;
-    }
-  };
-  auto fma_row = [&](int k, const float (&w)[8]) {
-    float xv[BG];
-    if constexpr (BG % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < BG; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(xs + k * BG + i);
-        xv[i] = v.x; xv[i + 1] = v.y; xv[i + 2] = v.z; xv[i + 3] = v.w;
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint4 (&raw)[U][RW] = buf[nb & 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = wave + kQkWaves * (nb * U + u);
+      if (r < nk) {
+        float w[8];
+        if constexpr (WBF16) {
+          const uint4 v = raw[u][0];
+          w[0] = bf_lo(v.x); w[1] = bf_hi(v.x); w[2] = bf_lo(v.y); w[3] = bf_hi(v.y);
+          w[4] = bf_lo(v.z); w[5] = bf_hi(v.z); w[6] = bf_lo(v.w); w[7] = bf_hi(v.w);
+        } else {
+          w[0] = __uint_as_float(raw[u][0].x); w[1] = __uint_as_float(raw[u][0].y);
+          w[2] = __uint_as_float(raw[u][0].z); w[3] = __uint_as_float(raw[u][0].w);
+          w[4] = __uint_as_float(raw[u][1].x); w[5] = __uint_as_float(raw[u][1].y);
+          w[6] = __uint_as_float(raw[u][1].z); w[7] = __uint_as_float(raw[u][1].w);
+        }
+        float xv[BG];
+        if constexpr (BG % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < BG; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(xs + r * BG + i);
+            xv[i] = v.x; xv[i + 1] = v.y; xv[i + 2] = v.z; xv[i + 3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < BG; ++i) xv[i] = xs[r * BG + i];
+        }
+#pragma unroll
+        for (int i = 0; i < BG; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv[i], w[j], acc[i][j]);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < BG; ++i) xv[i] = xs[k * BG + i];
     }
-#pragma unroll
-    for (int i = 0; i < BG; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv[i], w[j], acc[i][j]);
-  };
-
-  if (live) {
-    constexpr int U = BG >= 16 ? 4 : 8;  // rows in flight per lane
-    int k = wave;
-    for (; k + kQkWaves * (U - 1) < nk; k += kQkWaves * U) {
-      float w[U][8];
-#pragma unroll
-      for (int u = 0; u < U; ++u) load_row(k + kQkWaves * u, w[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) fma_row(k + kQkWaves * u, w[u]);
-    }
-    for (; k < nk; k += kQkWaves) {
-      float w[8];
-      load_row(k, w);
-      fma_row(k, w);
-    }
+    if (nb + 2 < NB) load(buf[nb & 1], nb + 2);
   }
   __syncthreads();  // xs is dead; the space becomes the cross-wave buffer
 
@@ -129,6 +166,8 @@ __global__ void __launch_bounds__(512) qk_proj_kernel(const float* __restrict__ 
   }
 }
 
+constexpr int kQkSumBatch = 32;  // partials loaded together per output
+
 template <bool KBF16>
 __global__ void __launch_bounds__(256) qk_finish_kernel(const float* __restrict__ part, int ks,
                                                         float* __restrict__ q, void* __restrict__ Kc,
@@ -139,8 +178,15 @@ __global__ void __launch_bounds__(256) qk_finish_kernel(const float* __restrict_
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long long)B * n2) return;
   const int b = (int)(i / n2), c = (int)(i - (long long)b * n2);
+  const size_t stride = (size_t)B * n2;
   float s = 0.f;
-  for (int k = 0; k < ks; ++k) s += part[(size_t)k * B * n2 + i];
+  for (int k = 0; k < ks; k += kQkSumBatch) {  // loads of a batch first, then the sum in order
+    float v[kQkSumBatch];
+#pragma unroll
+    for (int j = 0; j < kQkSumBatch; ++j) v[j] = k + j < ks ? part[(size_t)(k + j) * stride + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kQkSumBatch; ++j) s += v[j];
+  }
   int len = lengths[b];
   len = len < 0 ? 0 : (len > T_max ? T_max : len);
   if (c < d) {
@@ -153,21 +199,26 @@ __global__ void __launch_bounds__(256) qk_finish_kernel(const float* __restrict_
   if (c == 0) lengths_next[b] = len < T_max ? len + 1 : T_max;
 }
 
-bool make_step_plan(int B, int d, int ncu, size_t base, StepPlan* p) {
+bool make_step_plan(int B, int d, int ncu, bool w_bf16, size_t base, StepPlan* p) {
   if (B <= 0 || d <= 0 || d % 8 != 0) return false;
   p->bg = B >= 16 ? 16 : (B > 8 ? 16 : (B > 4 ? 8 : (B > 2 ? 4 : B)));
   const int ntile = (2 * d + kQkCols - 1) / kQkCols;
   const int bgroups = (B + p->bg - 1) / p->bg;
-  long long ks = ((long long)ncu + (long long)ntile * bgroups - 1) / ((long long)ntile * bgroups);
-  const int kmax = (d + 63) / 64;  // at least 64 rows (8 per wave) per workgroup
-  if (ks > kmax) ks = kmax;
-  if (ks < 1) ks = 1;
-  int kr = (int)((d + ks - 1) / ks);
-  kr = (kr + 7) / 8 * 8;
-  const int kr_cap = 16384 / p->bg;  // x rows staged in LDS: at most 64 KB
-  if (kr > kr_cap) kr = kr_cap;
-  p->kr = kr;
-  p->ks = (d + kr - 1) / kr;
+  // one round of workgroups where possible: two per compute unit for few
+  // sequences (short, load-bound blocks), one for many (their partial sums
+  // grow with B); the fewest batches per wave that fit
+  const long long target = (long long)ncu * (p->bg <= 4 ? 2 : 1);
+  const int rows1 = kQkWaves * (w_bf16 ? qk_batch_rows<true>() : qk_batch_rows<false>());
+  p->nb = 4;
+  for (int nb = 1; nb <= 4; nb *= 2) {
+    const long long ks = (d + (long long)rows1 * nb - 1) / ((long long)rows1 * nb);
+    if (ks * ntile * bgroups <= target) {
+      p->nb = nb;
+      break;
+    }
+  }
+  p->kr = rows1 * p->nb;
+  p->ks = (d + p->kr - 1) / p->kr;
   p->ntile = ntile;
   p->bgroups = bgroups;
   size_t off = (base + 255) & ~(size_t)255;
@@ -179,26 +230,37 @@ bool make_step_plan(int B, int d, int ncu, size_t base, StepPlan* p) {
   return true;
 }
 
-template <bool WBF16, int BG>
+template <bool WBF16, int BG, int NB>
 static hipError_t launch_proj(const StepPlan& p, const float* x, const void* WQ, const void* WK,
                               float* part, int B, int d, hipStream_t s) {
   constexpr int CB = BG < 4 ? BG : 4;
-  const size_t xs = (size_t)p.kr * BG * sizeof(float);
+  const size_t xs = (size_t)((qk_block_rows<WBF16, NB>() * BG + 511) / 512) * 512 * sizeof(float);
   const size_t red = (size_t)kQkWaves * CB * kQkCols * sizeof(float);
-  hipLaunchKernelGGL((qk_proj_kernel<WBF16, BG>), dim3(p.ntile, p.ks, p.bgroups), dim3(512),
-                     xs > red ? xs : red, s, x, WQ, WK, part, B, d, p.kr);
+  hipLaunchKernelGGL((qk_proj_kernel<WBF16, BG, NB>), dim3(p.ntile, p.ks, p.bgroups), dim3(512),
+                     xs > red ? xs : red, s, x, WQ, WK, part, B, d);
   return hipGetLastError();
+}
+
+template <bool WBF16, int BG>
+static hipError_t launch_proj_nb(const StepPlan& p, const float* x, const void* WQ, const void* WK,
+                                 float* part, int B, int d, hipStream_t s) {
+  switch (p.nb) {
+    case 1: return launch_proj<WBF16, BG, 1>(p, x, WQ, WK, part, B, d, s);
+    case 2: return launch_proj<WBF16, BG, 2>(p, x, WQ, WK, part, B, d, s);
+    case 4: return launch_proj<WBF16, BG, 4>(p, x, WQ, WK, part, B, d, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <bool WBF16>
 static hipError_t launch_proj_bg(const StepPlan& p, const float* x, const void* WQ, const void* WK,
                                  float* part, int B, int d, hipStream_t s) {
   switch (p.bg) {
-    case 1: return launch_proj<WBF16, 1>(p, x, WQ, WK, part, B, d, s);
-    case 2: return launch_proj<WBF16, 2>(p, x, WQ, WK, part, B, d, s);
-    case 4: return launch_proj<WBF16, 4>(p, x, WQ, WK, part, B, d, s);
-    case 8: return launch_proj<WBF16, 8>(p, x, WQ, WK, part, B, d, s);
-    case 16: return launch_proj<WBF16, 16>(p, x, WQ, WK, part, B, d, s);
+    case 1: return launch_proj_nb<WBF16, 1>(p, x, WQ, WK, part, B, d, s);
+    case 2: return launch_proj_nb<WBF16, 2>(p, x, WQ, WK, part, B, d, s);
+    case 4: return launch_proj_nb<WBF16, 4>(p, x, WQ, WK, part, B, d, s);
+    case 8: return launch_proj_nb<WBF16, 8>(p, x, WQ, WK, part, B, d, s);
+    case 16: return launch_proj_nb<WBF16, 16>(p, x, WQ, WK, part, B, d, s);
   }
   return hipErrorInvalidValue;
 }
