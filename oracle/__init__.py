@@ -38,5 +38,7 @@ from .mha import (  # noqa: F401
     prefill_loop,
     generate_step,
     append_rows,
+    multi_query_attention,
+    multi_query_cost,
     err_rel,
 )

@@ -273,3 +273,46 @@ def append_rows(K_cache, k_new, lengths):
             else:
                 K[b, n] = k_new[b]
     return K
+
+
+# ----------------------------------------------------------------------------
+# many queries over one context: shared-context cross-attention, prompt phase
+
+def multi_query_attention(Q, K, V, limits, H: int, dh: int, scale: float) -> np.ndarray:
+    """Standard multi-head attention of n queries over ONE key/value context.
+
+    Q [n, H*dh]; K, V [T, H*dh] explicit (float64 values); limits [n] or
+    None: query i attends rows [0, limit_i) (clamped to [0, T]; None = all
+    T rows).  A query with no rows yields zeros.  Returns [n, H, dh].
+    With every limit T this is cross-attention of n decoder queries over one
+    shared encoder context; with limit_i = t0 + i + 1 it is the causal
+    attention of a prompt's tokens (each token sees itself and all earlier
+    rows), the prompt phase of the Slim Attention article (section "K-Cache
+    is All You Need": queries and keys of all prompt tokens computed in
+    parallel)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = cache_to_f64(np.asarray(K))
+    V = np.asarray(V, dtype=np.float64)
+    n, T = Q.shape[0], K.shape[0]
+    lim = np.full(n, T) if limits is None else np.asarray(limits)
+    o = np.zeros((n, H, dh))
+    for i in range(n):
+        r = _clamp_len(lim[i], T)
+        if r == 0:
+            continue
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = scale * (K[:r, c] @ Q[i, c])
+            e = np.exp(s - s.max())
+            o[i, h] = (e / e.sum()) @ V[:r, c]
+    return o
+
+
+def multi_query_cost(n: int, H: int, T: int, d: int) -> dict:
+    """Multiply-accumulate counts of the two generation options of the Slim
+    Attention article (section "K-Cache is All You Need") for n queries over
+    a T-row context, projections included: option 1 forms V = K.W_KV
+    (T d^2) and multiplies the softmax by it (n T d); option 2 multiplies the
+    softmax of every head by all d columns of K (n H T d) and the n H rows by
+    W_KV's head slices (n d^2)."""
+    return {"opt1": T * d * d + n * T * d, "opt2": n * H * T * d + n * d * d}

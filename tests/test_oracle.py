@@ -449,3 +449,88 @@ def test_step_pin_catches_planted_mistakes(mutant):
     want = _causal_excl_loop(X, W_Q, W_K, W_V, H, dh, 1 / math.sqrt(dh))
     got, _, _ = _run_steps(mutant, X, W_Q, W_K, W_V, H, dh, T=n + 1)
     assert _rel(got, want) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# many queries over one context
+
+def _causal_incl_loop(Q, K, V, H, dh, scale, t0=0):
+    """Prompt token i (absolute row t0 + i) attends rows 0..t0+i, scalar loops."""
+    n = Q.shape[0]
+    out = np.zeros((n, H, dh))
+    for i in range(n):
+        r = t0 + i + 1
+        for h in range(H):
+            s = [scale * sum(Q[i, h * dh + j] * K[t, h * dh + j] for j in range(dh)) for t in range(r)]
+            m = max(s)
+            e = [math.exp(v - m) for v in s]
+            z = sum(e)
+            for j in range(dh):
+                out[i, h, j] = sum(e[t] * V[t, h * dh + j] for t in range(r)) / z
+    return out
+
+
+def test_multi_query_causal_matches_loop():
+    rng = np.random.default_rng(21)
+    H, dh, T, t0 = 2, 3, 9, 4
+    d = H * dh
+    Q = rng.standard_normal((T - t0, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    lim = t0 + np.arange(T - t0) + 1
+    got = oracle.multi_query_attention(Q, K, V, lim, H, dh, 0.7)
+    assert _rel(got, _causal_incl_loop(Q, K, V, H, dh, 0.7, t0)) < 1e-12
+
+
+def test_multi_query_shared_context_is_decode_with_broadcast_cache():
+    rng = np.random.default_rng(22)
+    H, dh, T, n = 3, 4, 11, 5
+    d = H * dh
+    Q = rng.standard_normal((n, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    lim = np.array([11, 0, 3, 20, 1])
+    got = oracle.multi_query_attention(Q, K, V, lim, H, dh, 0.5)
+    want = oracle.mha_decode_loop(Q, np.broadcast_to(K, (n, T, d)), np.broadcast_to(V, (n, T, d)), lim,
+                                  H, dh, 0.5)
+    assert _rel(got, want) < 1e-12
+    assert np.abs(got[1]).max() == 0
+    assert np.abs(got[4] - V[0].reshape(H, dh)).max() < 1e-14       # one row: its value row
+    full = oracle.multi_query_attention(Q, K, V, None, H, dh, 0.5)
+    assert np.array_equal(full[0], got[0])
+
+
+def test_multi_query_options_agree():
+    """Both Slim options (V = K W_KV materialised, or softmax times K then
+    W_KV) reproduce the explicit-V definition for many queries."""
+    rng = np.random.default_rng(23)
+    H, dh, T, n = 2, 4, 10, 6
+    d = H * dh
+    W_K, W_V = _step_weights(24, d)[1], rng.standard_normal((d, d)) / math.sqrt(d)
+    X = rng.standard_normal((T, d))
+    K = X @ W_K
+    Q = rng.standard_normal((n, d))
+    lim = np.array([10, 4, 7, 1, 10, 9])
+    want = oracle.multi_query_attention(Q, K, X @ W_V, lim, H, dh, 0.5)
+    Wkv = oracle.wkv(W_K, W_V)
+    opt1 = oracle.multi_query_attention(Q, K, K @ Wkv, lim, H, dh, 0.5)
+    # option 2 written out: per head, softmax over all d columns of K, then the head slice of W_KV
+    opt2 = np.zeros_like(want)
+    for i in range(n):
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = 0.5 * (K[:lim[i], c] @ Q[i, c])
+            p = np.exp(s - s.max())
+            opt2[i, h] = (p / p.sum()) @ K[:lim[i]] @ Wkv[:, c]
+    assert _rel(opt1, want) < 1e-10 and _rel(opt2, want) < 1e-10
+
+
+def test_multi_query_cost_model():
+    c = oracle.multi_query_cost(1, 32, 131072, 4096)                 # one decode query: option 2
+    assert c["opt2"] < c["opt1"]
+    c = oracle.multi_query_cost(2048, 12, 2048, 768)                 # a whole prompt: option 1
+    assert c["opt1"] < c["opt2"]
+    # the crossover for a decode-sized context sits near n ~ d / H queries
+    n_star = next(n for n in range(1, 10000) if (lambda c: c["opt1"] < c["opt2"])(
+        oracle.multi_query_cost(n, 20, 1500, 1280)))
+    assert 40 <= n_star <= 80
