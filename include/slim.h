@@ -204,6 +204,51 @@ slim_status_t slim_step(const float* x,
                         hipStream_t stream);
 
 /*
+ * slim_multi_query -- n queries over ONE context of T key rows (Slim
+ * Attention article, section "K-Cache is All You Need": only K is kept and
+ * V = K.W_KV; the first option forms V and multiplies the softmax by it,
+ * the second multiplies the softmax by K first and the result by W_KV).
+ * Two uses: cross-attention of n decoder queries over one shared encoder
+ * context (limits NULL), and the prompt phase, where the prompt's n tokens
+ * attend causally over its own rows (limits[i] = t0 + i + 1).
+ *   Q       : device float32 [n, d], unscaled queries
+ *   K       : device bf16 [T, d], the context's key rows
+ *   limits  : device int32 [n] or NULL: query i attends rows
+ *             [0, min(max(limits[i], 0), T)); NULL means all T rows.  A query
+ *             with no rows gets a zero output row.
+ *   W_KV    : device [d, d] in w_dt
+ *   out     : device float32 [n, H, dh]:
+ *               out[i,h,:] = softmax_t(scale * Q[i,h-cols] . K[t,h-cols]) . K[t,:] . W_KV[:, h-cols]
+ *   option  : 1 (form V = K.W_KV in the workspace, rounded to bf16, then the
+ *             softmax times V), 2 (softmax times K on all d columns, then
+ *             W_KV), 0 = the cheaper by multiply-accumulate count:
+ *             option 1 costs T d^2 + n T d, option 2 n H T d + n d^2
+ *             (slim_multi_query_option returns the choice).
+ *   workspace : at least slim_multi_query_workspace_bytes(...) bytes for the
+ *             same shape and option, 16-byte aligned.
+ * Arithmetic: scores on bf16 MFMA with Q split into high and low bf16 parts
+ * (fp32 accumulation); softmax in fp32; softmax weights rounded to bf16 for
+ * the MFMA product with K (or V); merge and projection in fp32.
+ * Supported: k_dt bf16; w_dt bf16 or f32 (option 1: bf16 only); dh in
+ * {64, 128}; d a multiple of 128.  Alignment: Q, K, W_KV, workspace 16
+ * bytes; out, limits 4 bytes.
+ * Errors: SLIM_ERR_INVALID (null pointers, sizes <= 0, option outside 0..2,
+ * scale not finite, misalignment), SLIM_ERR_UNSUPPORTED, SLIM_ERR_WORKSPACE,
+ * SLIM_ERR_HIP.
+ */
+int slim_multi_query_option(int n, int H, int dh, int T);
+size_t slim_multi_query_workspace_bytes(int n, int H, int dh, int T, slim_dtype_t k_dt,
+                                        slim_dtype_t w_dt, int option);
+slim_status_t slim_multi_query(const float* Q,
+                               const void* K, slim_dtype_t k_dt,
+                               const int32_t* limits,
+                               const void* W_KV, slim_dtype_t w_dt,
+                               float* out,
+                               int n, int H, int dh, int T, float scale, int option,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * mha_decode_kv -- comparator: standard MHA decode over explicit K and V
  * caches (the baseline the Slim Attention article halves), same conventions
  * as slim_decode with V_cache [B, T_max, d] in kv_dt in place of W_KV:

@@ -47,6 +47,12 @@ lib.slim_step_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.slim_step.restype = _i
 lib.slim_step.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _sz,
                           _vp]
+lib.slim_multi_query_option.restype = _i
+lib.slim_multi_query_option.argtypes = [_i, _i, _i, _i]
+lib.slim_multi_query_workspace_bytes.restype = _sz
+lib.slim_multi_query_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+lib.slim_multi_query.restype = _i
+lib.slim_multi_query.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 lib.mha_decode_kv_workspace_bytes.restype = _sz
 lib.mha_decode_kv_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.mha_decode_kv.restype = _i
@@ -203,6 +209,36 @@ def step(x, W_Q, W_K, K_cache, lengths, lengths_next, W_KV, out, H, dh, scale=No
     _check(lib.slim_step(_dev(x), _dev(W_Q), _dev(W_K), _dt(W_Q), _dev(K_cache), _dt(K_cache),
                          _dev(lengths), _dev(lengths_next), _dev(W_KV), _dt(W_KV), _dev(out),
                          B, H, dh, T_max, a[11], _dev(ws), ws.numel(), _stream(stream)), "slim_step")
+
+
+def multi_query_option(n: int, H: int, dh: int, T: int) -> int:
+    return int(lib.slim_multi_query_option(n, H, dh, T))
+
+
+def multi_query_workspace_bytes(n: int, H: int, dh: int, T: int, w_dtype, option: int = 0) -> int:
+    code = w_dtype if isinstance(w_dtype, int) else _dt_of(w_dtype)
+    return int(lib.slim_multi_query_workspace_bytes(n, H, dh, T, BF16, code, option))
+
+
+def multi_query(Q, K, W_KV, out, H, dh, limits=None, scale=None, option=0, ws=None, stream=None) -> None:
+    """n queries over one context (see slim_multi_query in include/slim.h):
+    Q [n, d] float32, K [T, d] bf16, W_KV [d, d], out [n, H, dh] float32,
+    limits int32 [n] on the device or None (all rows)."""
+    n, d = Q.shape
+    T = K.shape[0]
+    if K.shape != (T, d) or W_KV.shape != (d, d) or out.shape != (n, H, dh) or d != H * dh:
+        raise ValueError("shape mismatch")
+    if limits is not None and limits.shape != (n,):
+        raise ValueError("limits must be [n]")
+    torch = _torch()
+    if Q.dtype != torch.float32 or out.dtype != torch.float32:
+        raise TypeError("Q and out are float32")
+    if ws is None:
+        ws = workspace(multi_query_workspace_bytes(n, H, dh, T, W_KV.dtype, option), Q.device)
+    scale = 1.0 / math.sqrt(dh) if scale is None else float(scale)
+    _check(lib.slim_multi_query(_dev(Q), _dev(K), _dt(K), None if limits is None else _dev(limits),
+                                _dev(W_KV), _dt(W_KV), _dev(out), n, H, dh, T, scale, int(option), _dev(ws),
+                                ws.numel(), _stream(stream)), "slim_multi_query")
 
 
 def mha_kv_workspace_bytes(B: int, H: int, dh: int, T_max: int, dtype) -> int:

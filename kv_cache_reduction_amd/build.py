@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libslim.so")
 
 HIP_SOURCES = ["api.hip", "attend_bf16.hip", "attend_f32.hip", "finish.hip", "mha_kv.hip",
-               "prefill.hip", "probe.hip", "step.hip"]
+               "multi.hip", "prefill.hip", "probe.hip", "step.hip"]
 CPP_SOURCES = ["wkv_host.cpp"]
 # The bf16 attend kernel never sees NaN in the rows it reads (it only takes
 # maxima of finite scores and -inf); without this flag every fmaxf first

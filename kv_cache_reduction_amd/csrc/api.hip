@@ -10,6 +10,7 @@
 #include "slim.h"
 #include "internal.hpp"
 #include "step.hpp"
+#include "multi.hpp"
 
 namespace slim {
 
@@ -299,6 +300,54 @@ slim_status_t slim_step(const float* x, const void* W_Q, const void* W_K, slim_d
   if (e != hipSuccess) return SLIM_ERR_HIP;
   a.q = reinterpret_cast<const float*>(ws + sp.off_q);
   return decode_launch(kFull, plan, a, stream) == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
+}
+
+static slim_status_t multi_shape_ok(int n, int H, int dh, int T, slim_dtype_t k_dt, slim_dtype_t w_dt,
+                                    int option) {
+  if (n <= 0 || H <= 0 || dh <= 0 || T <= 0) return SLIM_ERR_INVALID;
+  if (option < 0 || option > 2) return SLIM_ERR_INVALID;
+  if (k_dt != SLIM_BF16 || (w_dt != SLIM_BF16 && w_dt != SLIM_F32)) return SLIM_ERR_UNSUPPORTED;
+  if ((dh != 64 && dh != 128) || (H * dh) % 128 != 0 || H * dh > 65536) return SLIM_ERR_UNSUPPORTED;
+  if (n > (1 << 20) || T > 4000000 || (long long)H * ((n + 31) / 32) > 65535) return SLIM_ERR_UNSUPPORTED;
+  return SLIM_OK;
+}
+
+int slim_multi_query_option(int n, int H, int dh, int T) {
+  if (n <= 0 || H <= 0 || dh <= 0 || T <= 0) return 0;
+  const double d = (double)H * dh;
+  const double o1 = (double)T * d * d + (double)n * T * d, o2 = (double)n * H * T * d + (double)n * d * d;
+  return o1 < o2 ? 1 : 2;
+}
+
+size_t slim_multi_query_workspace_bytes(int n, int H, int dh, int T, slim_dtype_t k_dt, slim_dtype_t w_dt,
+                                        int option) {
+  if (multi_shape_ok(n, H, dh, T, k_dt, w_dt, option) != SLIM_OK) return 0;
+  int ncu = 0;
+  if (device_cus(&ncu) != 0) return 0;
+  MultiPlan p;
+  if (!make_multi_plan(n, H, dh, T, option, w_dt == SLIM_BF16, ncu, &p)) return 0;
+  return p.bytes;
+}
+
+slim_status_t slim_multi_query(const float* Q, const void* K, slim_dtype_t k_dt, const int32_t* limits,
+                               const void* W_KV, slim_dtype_t w_dt, float* out, int n, int H, int dh, int T,
+                               float scale, int option, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (!Q || !K || !W_KV || !out || !workspace) return SLIM_ERR_INVALID;
+  if (!std::isfinite(scale)) return SLIM_ERR_INVALID;
+  slim_status_t st = multi_shape_ok(n, H, dh, T, k_dt, w_dt, option);
+  if (st != SLIM_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(W_KV) || !aligned16(workspace) || ((uintptr_t)out & 3u) ||
+      ((uintptr_t)limits & 3u))
+    return SLIM_ERR_INVALID;
+  int ncu = 0;
+  if (device_cus(&ncu) != 0) return SLIM_ERR_HIP;
+  MultiPlan plan;
+  if (!make_multi_plan(n, H, dh, T, option, w_dt == SLIM_BF16, ncu, &plan)) return SLIM_ERR_UNSUPPORTED;
+  if (workspace_bytes < plan.bytes) return SLIM_ERR_WORKSPACE;
+  hipError_t e = launch_multi(plan, Q, K, limits, W_KV, w_dt == SLIM_BF16, out, n, H, dh, T, scale,
+                              static_cast<char*>(workspace), stream);
+  return e == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 static slim_status_t kv_shape_ok(int B, int H, int dh, int T_max, slim_dtype_t kv_dt) {

@@ -21,6 +21,7 @@
 //          result does not depend on scheduling.
 #include "common.hpp"
 #include "internal.hpp"
+#include "multi.hpp"
 
 namespace slim {
 
@@ -32,7 +33,7 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
                                                             const float* __restrict__ ml,
                                                             const void* __restrict__ W,
                                                             float* __restrict__ part, int B, int H, int d,
-                                                            int T_max, int nch, int nslots) {
+                                                            int T_max, int nch, int nslots, int fixed_ns) {
   // projection: thread t covers JW output columns (group jq = t % JQ) over the
   // rows of subset t / JQ
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;  // column groups per head
@@ -82,8 +83,13 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
     }
   }
 
-  lengths_prefix(lengths, B, T_max, pre, tmp);
-  const int Ts = chunk_tokens(pre[B] > 0 ? pre[B] : 1, nch);
+  // slots of sequence b: the chunks its rows fall in (decode), or a fixed
+  // count per row, slot = b * fixed_ns + split (many queries over one context)
+  int Ts = 1;
+  if (fixed_ns == 0) {
+    lengths_prefix(lengths, B, T_max, pre, tmp);
+    Ts = chunk_tokens(pre[B] > 0 ? pre[B] : 1, nch);
+  }
 
   // merged rows u[bb][r] of head h, rows [r0, r0 + nr): G sequences at a
   // time, 256/G threads each (C4 float4 columns x nss slot subsets).  Each
@@ -100,9 +106,16 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float m = kNegInf, l = 0.f;
     bool bad = false;
-    if (bb < nb && pre[b + 1] > pre[b]) {
-      const int s0 = pre[b], s1 = pre[b + 1];
-      const int cf = s0 / Ts, ns = (s1 - 1) / Ts - cf + 1, slot0 = cf + b;
+    if (bb < nb && (fixed_ns > 0 || pre[b + 1] > pre[b])) {
+      int ns, slot0;
+      if (fixed_ns > 0) {
+        ns = fixed_ns;
+        slot0 = b * fixed_ns;
+      } else {
+        const int s0 = pre[b], s1 = pre[b + 1], cf = s0 / Ts;
+        ns = (s1 - 1) / Ts - cf + 1;
+        slot0 = cf + b;
+      }
       const bool cols = 4 * c4 < nr;
       const float* src = U + ((size_t)h * nslots + slot0) * d + r0 + 4 * c4;
       const float* mls = ml + (size_t)slot0 * 2 * H + h;
@@ -217,7 +230,7 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(const float* __restric
 }
 
 template <int DH, bool WBF16, int PR>
-static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_ns, hipStream_t s) {
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;
   constexpr int NRS = 256 / JQ;
   constexpr int NSS = 256 / (PR / 4);
@@ -225,10 +238,10 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   const float* U = reinterpret_cast<const float*>(a.ws + pl.off_U);
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
-  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * NSS + (size_t)a.B + 1) * 4;
+  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * NSS + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
   hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR>),
                      dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), lds, s, a.lengths,
-                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots);
+                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;
@@ -238,28 +251,33 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
 }
 
 template <int DH>
-static hipError_t launch_w(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_w(const DecodePlan& pl, const DecodeArgs& a, int fixed_ns, hipStream_t s) {
   constexpr int big = proj_rows(DH, true), small = proj_rows(DH, false);
   if (pl.proj_rows == big)
-    return a.w_bf16 ? launch_t<DH, true, big>(pl, a, s) : launch_t<DH, false, big>(pl, a, s);
+    return a.w_bf16 ? launch_t<DH, true, big>(pl, a, fixed_ns, s) : launch_t<DH, false, big>(pl, a, fixed_ns, s);
   if (pl.proj_rows == small)
-    return a.w_bf16 ? launch_t<DH, true, small>(pl, a, s) : launch_t<DH, false, small>(pl, a, s);
+    return a.w_bf16 ? launch_t<DH, true, small>(pl, a, fixed_ns, s)
+                    : launch_t<DH, false, small>(pl, a, fixed_ns, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_finish_fixed(const DecodePlan& pl, const DecodeArgs& a, int fixed_ns, hipStream_t s) {
+  switch (a.dh) {
+    case 1: return launch_w<1>(pl, a, fixed_ns, s);
+    case 2: return launch_w<2>(pl, a, fixed_ns, s);
+    case 4: return launch_w<4>(pl, a, fixed_ns, s);
+    case 8: return launch_w<8>(pl, a, fixed_ns, s);
+    case 16: return launch_w<16>(pl, a, fixed_ns, s);
+    case 32: return launch_w<32>(pl, a, fixed_ns, s);
+    case 64: return launch_w<64>(pl, a, fixed_ns, s);
+    case 128: return launch_w<128>(pl, a, fixed_ns, s);
+    case 256: return launch_w<256>(pl, a, fixed_ns, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_finish(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
-  switch (a.dh) {
-    case 1: return launch_w<1>(pl, a, s);
-    case 2: return launch_w<2>(pl, a, s);
-    case 4: return launch_w<4>(pl, a, s);
-    case 8: return launch_w<8>(pl, a, s);
-    case 16: return launch_w<16>(pl, a, s);
-    case 32: return launch_w<32>(pl, a, s);
-    case 64: return launch_w<64>(pl, a, s);
-    case 128: return launch_w<128>(pl, a, s);
-    case 256: return launch_w<256>(pl, a, s);
-  }
-  return hipErrorInvalidValue;
+  return launch_finish_fixed(pl, a, 0, s);
 }
 
 }  // namespace slim

@@ -1,0 +1,415 @@
+// Many queries over one context, on MFMA: shared-context cross-attention
+// (n decoder queries over one encoder K) and the causal prompt phase (a
+// prompt's n tokens over its own K rows).  Slim Attention article,
+// localbendi.com, section "K-Cache is All You Need": only K is kept; the
+// values follow from V = K.W_KV, either formed first (option 1) or applied
+// after the softmax has been multiplied by K (option 2).
+//
+// multi_attend<DH, QW, OPT>  grid (column blocks, H x query groups, T splits),
+// QW waves of 64 lanes; wave w owns 32 queries of head h.
+//  * Tiles of 32 context rows travel global -> registers -> LDS (double
+//    buffered, one barrier per tile): head h's DH key columns for the scores
+//    and the value block: 128 columns of K (option 2) or head h's DH columns
+//    of V (option 1).  All waves of the workgroup share the tile.
+//  * Scores S = Q_h . K_h^T on 32x32x8 bf16 MFMA with Q split into bf16 high
+//    and low parts (two MFMAs per step), so the products keep about 16 bits
+//    of Q; fp32 accumulation.  The reduction over the head's DH dimensions is
+//    ordered so that a lane's B operand is one 8-byte LDS read of its row:
+//    lanes 0-31 take dimensions [0, DH/2), lanes 32-63 [DH/2, DH), four per
+//    step, and the A operand (Q, in registers for the whole kernel) follows
+//    the same order.
+//  * The 32x32 score tile goes through a private LDS buffer from the MFMA
+//    result layout (lane = context row) to the A-operand layout (lane =
+//    query, 16 rows each, halves joined by a lane swap), where the online
+//    softmax runs: rows past a query's limit are -inf; lazy rescaling keeps
+//    a reference max m (log2 units; Q is pre-scaled by scale*log2 e) that
+//    moves only when a score exceeds it by more than 8, so weights stay
+//    below 2^8; the accumulator rows are then rescaled through LDS.
+//  * P (bf16) . value block on 32x32x8 MFMA, B operands by transpose reads
+//    (ds_read_b64_tr_b16) of the tile rows.
+//  * Option 2 writes unnormalised partial rows U[h, q*nsplit + split, cols]
+//    and (column block 0) m and the normaliser l, the layout the decode
+//    finish merges and projects by W_KV.  Option 1 (one split) writes the
+//    normalised output rows directly.
+#include "common.hpp"
+#include "internal.hpp"
+#include "multi.hpp"
+
+namespace slim {
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_m;
+
+constexpr int kMTile = 32;              // context rows per tile
+constexpr float kMultiSlack = 8.f;      // log2 units
+constexpr int kSPitch = 33;             // floats per row of the private score buffer
+
+struct MultiParams {
+  const float* Q;          // [n, d]
+  const uint16_t* K;       // [T, d] bf16
+  const uint16_t* Vs;      // value rows [T, d] bf16: K (option 2) or V (option 1)
+  const int32_t* limits;   // [n] or null (all T rows)
+  float* U;                // option 2: [H][n * nsplit][d]
+  float* ml;               // option 2: [n * nsplit][2][H]
+  float* out;              // option 1: [n][H][DH]
+  int n, H, d, T, nsplit, Ts, nslots;
+  float qscale;
+};
+
+// The pair {x of lane l, x of lane l^32} in every lane (in some order):
+// their max or sum is the reduction over the two halves of the wave.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int DH, int OPT>
+struct MultiShape {
+  static constexpr int NCW = OPT == 2 ? 128 : DH;     // value columns per workgroup
+  static constexpr int NCT = NCW / 32;                // 32-column MFMA tiles per wave
+  static constexpr int SP = DH * 2 + 8;               // bytes per score row in LDS
+  static constexpr int VP = NCW * 2 + 16;             // bytes per value row in LDS
+  static constexpr int SCH = kMTile * DH / 8;         // 16-byte chunks of the score part
+  static constexpr int VCH = kMTile * NCW / 8;        // 16-byte chunks of the value part
+  static constexpr int TILE = kMTile * (SP + VP);     // bytes per tile buffer
+};
+
+template <int DH, int QW, int OPT>
+__global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
+  using S = MultiShape<DH, OPT>;
+  constexpr int NT = 64 * QW;
+  constexpr int CPT = (S::SCH + S::VCH + NT - 1) / NT;  // chunks per thread and tile
+  extern __shared__ __attribute__((aligned(16))) char msm[];
+  char* tiles = msm;                                               // [2][TILE]
+  float* sbuf = reinterpret_cast<float*>(msm + 2 * S::TILE);       // [QW][32][kSPitch]
+  float* rowv = sbuf + QW * 32 * kSPitch;                          // [QW][32]
+  int* lim_max = reinterpret_cast<int*>(rowv + QW * 32);           // [1]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, m = lane & 31;
+  const int nqg = (p.n + 32 * QW - 1) / (32 * QW);
+  const int h = blockIdx.y / nqg, qg = blockIdx.y - h * nqg;
+  const int split = blockIdx.z;
+  const int d = p.d;
+  const int c0 = OPT == 2 ? blockIdx.x * S::NCW : h * DH;  // first value column
+  const int q = (qg * QW + wave) * 32 + m;                 // this lane's query row
+  const bool qok = q < p.n;
+
+  // query limits: this lane's row, and the workgroup maximum (tiles stop there)
+  int lim = 0;
+  if (qok) {
+    lim = p.limits ? p.limits[q] : p.T;
+    lim = lim < 0 ? 0 : (lim > p.T ? p.T : lim);
+  }
+  if (tid == 0) *lim_max = 0;
+  __syncthreads();
+  if (hh == 0 && lim > 0) atomicMax(lim_max, lim);
+  __syncthreads();
+  const int t_begin = split * p.Ts;
+  const int t_end = min(min(p.T, t_begin + p.Ts), *lim_max);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kMTile - 1) / kMTile : 0;
+
+  // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
+  // order: step k takes dimensions hh*DH/2 + 4k .. +3
+  s16x4 qh[DH / 8], ql[DH / 8];
+  {
+    const float* qr = p.Q + (size_t)(qok ? q : 0) * d + h * DH + hh * (DH / 2);
+#pragma unroll
+    for (int k = 0; k < DH / 8; ++k) {
+      const float4 v = qok ? *reinterpret_cast<const float4*>(qr + 4 * k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+      split_bf16(v.x * p.qscale, h0, l0);
+      split_bf16(v.y * p.qscale, h1, l1);
+      split_bf16(v.z * p.qscale, h2, l2);
+      split_bf16(v.w * p.qscale, h3, l3);
+      qh[k] = s16x4{(short)h0, (short)h1, (short)h2, (short)h3};
+      ql[k] = s16x4{(short)l0, (short)l1, (short)l2, (short)l3};
+    }
+  }
+
+  // tile loads: chunk c < SCH is score row c / (DH/8), 8 columns at 8*(c % (DH/8));
+  // the rest are value rows.  Rows past T are clamped (masked later).
+  uint4 stage[CPT];
+  auto load_tile = [&](int tb) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c < S::SCH) {
+        const int r = c / (DH / 8), k8 = c - r * (DH / 8);
+        const int row = min(tb + r, p.T - 1);
+        v = *reinterpret_cast<const uint4*>(p.K + (size_t)row * d + h * DH + 8 * k8);
+      } else if (c < S::SCH + S::VCH) {
+        const int cc = c - S::SCH, r = cc / (S::NCW / 8), k8 = cc - r * (S::NCW / 8);
+        const int row = min(tb + r, p.T - 1);
+        const int col = min(c0 + 8 * k8, d - 8);
+        v = *reinterpret_cast<const uint4*>(p.Vs + (size_t)row * d + col);
+      }
+      stage[i] = v;
+    }
+  };
+  auto store_tile = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i;
+      if (c < S::SCH) {
+        const int r = c / (DH / 8), k8 = c - r * (DH / 8);
+        *reinterpret_cast<uint2*>(buf + r * S::SP + 16 * k8) = make_uint2(stage[i].x, stage[i].y);
+        *reinterpret_cast<uint2*>(buf + r * S::SP + 16 * k8 + 8) = make_uint2(stage[i].z, stage[i].w);
+      } else if (c < S::SCH + S::VCH) {
+        const int cc = c - S::SCH, r = cc / (S::NCW / 8), k8 = cc - r * (S::NCW / 8);
+        *reinterpret_cast<uint4*>(buf + kMTile * S::SP + r * S::VP + 16 * k8) = stage[i];
+      }
+    }
+  };
+
+  float* sb = sbuf + wave * 32 * kSPitch;
+  float* rv = rowv + wave * 32;
+  // transpose-read offset of the value part: lane L reads 4 columns
+  // 32s + 16*((L/16)%2) + 4*(L%4) of row 8k + 4*(L/32) + (L%16)/4; the
+  // 16-lane transpose leaves lane l with column 32s + l%32 of rows
+  // 8k + 4*(l/32) .. +3
+  const int tr_off = kMTile * S::SP + (4 * (lane >> 5) + ((lane & 15) >> 2)) * S::VP +
+                     (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+  f32x16 acc[S::NCT];
+#pragma unroll
+  for (int s = 0; s < S::NCT; ++s) acc[s] = f32x16{0};
+  float m_ref = kNegInf, l_half = 0.f;
+
+  if (ntiles > 0) load_tile(t_begin);
+  for (int it = 0; it < ntiles; ++it) {
+    char* buf = tiles + (it & 1) * S::TILE;
+    store_tile(buf);
+    __syncthreads();
+    const int tb = t_begin + it * kMTile;
+    if (it + 1 < ntiles) load_tile(tb + kMTile);
+
+    // scores of the tile (MFMA result layout: lane = row m of column l%32)
+    f32x16 sc = f32x16{0};
+    {
+      const char* srow = buf + m * S::SP + hh * DH;  // this lane's context row, its half
+#pragma unroll
+      for (int k = 0; k < DH / 8; ++k) {
+        const s16x4 b = *reinterpret_cast<const s16x4*>(srow + 8 * k);
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(qh[k], b, sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ql[k], b, sc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sb[(8 * (i >> 2) + 4 * hh + (i & 3)) * kSPitch + m] = sc[i];
+    // A-operand layout: row m, context rows 8k + 4*hh + j
+    float v[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 8 * k + 4 * hh + j;
+        const float x = sb[m * kSPitch + t];
+        v[k][j] = (tb + t < min(lim, t_end)) ? x : kNegInf;
+      }
+    float mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, v[k][j]);
+    mx = pair_max(mx);
+    const bool up = mx > m_ref + kMultiSlack;
+    if (__builtin_amdgcn_ballot_w64(up)) {  // some row moves its reference: rescale through LDS
+      const float nref = up ? mx : m_ref;
+      const float alpha = up ? (m_ref == kNegInf ? 0.f : fast_exp2(m_ref - nref)) : 1.f;
+      if (hh == 0) rv[m] = alpha;
+      l_half *= alpha;
+      m_ref = nref;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float a = rv[8 * (i >> 2) + 4 * hh + (i & 3)];
+#pragma unroll
+        for (int s = 0; s < S::NCT; ++s) acc[s][i] *= a;
+      }
+    }
+    s16x4 pa[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = v[k][j] == kNegInf ? 0.f : fast_exp2(v[k][j] - m_ref);
+        l_half += e[j];
+      }
+      pa[k] = s16x4{(short)f32_to_bf16_rne(e[0]), (short)f32_to_bf16_rne(e[1]),
+                    (short)f32_to_bf16_rne(e[2]), (short)f32_to_bf16_rne(e[3])};
+    }
+    // P . value block
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const lds_s16x4_m* a0 =
+          (const lds_s16x4_m*)(size_t)((uint32_t)(uintptr_t)(buf + tr_off) + (uint32_t)(8 * k * S::VP));
+#pragma unroll
+      for (int s = 0; s < S::NCT; ++s) {
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_m*>(a0 + 8 * s));
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(pa[k], b, acc[s], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_row = pair_sum(l_half);
+  const int qbase = (qg * QW + wave) * 32;
+  if constexpr (OPT == 2) {
+    const int slot_of = p.nsplit;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * hh + (i & 3), qq = qbase + r;
+      if (qq >= p.n) continue;
+      float* dst = p.U + ((size_t)h * p.nslots + (size_t)qq * slot_of + split) * d;
+#pragma unroll
+      for (int s = 0; s < S::NCT; ++s) {
+        const int col = c0 + 32 * s + m;
+        if (col < d) dst[col] = acc[s][i];
+      }
+    }
+    if (blockIdx.x == 0 && hh == 0 && qok) {
+      float* mls = p.ml + (size_t)(q * slot_of + split) * 2 * p.H;
+      mls[h] = m_ref;
+      mls[p.H + h] = l_row;
+    }
+  } else {
+    __syncthreads();  // rv is reused for the normalisers
+    if (hh == 0) rv[m] = l_row;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * hh + (i & 3), qq = qbase + r;
+      if (qq >= p.n) continue;
+      const float lr = rv[r];
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      float* dst = p.out + ((size_t)qq * p.H + h) * DH;
+#pragma unroll
+      for (int s = 0; s < S::NCT; ++s) dst[32 * s + m] = acc[s][i] * inv;
+    }
+  }
+}
+
+template <int DH, int QW, int OPT>
+static hipError_t launch_mq(const MultiPlan& pl, const MultiParams& mp, hipStream_t s) {
+  using S = MultiShape<DH, OPT>;
+  const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * kSPitch * 4 + (size_t)QW * 32 * 4 + 16;
+  auto kern = multi_attend_kernel<DH, QW, OPT>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int nqg = (mp.n + 32 * QW - 1) / (32 * QW);
+  const int ncb = OPT == 2 ? (mp.d + S::NCW - 1) / S::NCW : 1;
+  hipLaunchKernelGGL(kern, dim3(ncb, mp.H * nqg, pl.nsplit), dim3(64 * QW), lds, s, mp);
+  return hipGetLastError();
+}
+
+template <int DH, int OPT>
+static hipError_t launch_mq_qw(const MultiPlan& pl, const MultiParams& mp, hipStream_t s) {
+  switch (pl.qw) {
+    case 1: return launch_mq<DH, 1, OPT>(pl, mp, s);
+    case 2: return launch_mq<DH, 2, OPT>(pl, mp, s);
+    case 4: return launch_mq<DH, 4, OPT>(pl, mp, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool make_multi_plan(int n, int H, int dh, int T, int method, bool w_bf16, int ncu, MultiPlan* p) {
+  const long long d = (long long)H * dh;
+  if (n <= 0 || H <= 0 || T <= 0 || (dh != 64 && dh != 128) || d % 128 != 0 || d > 65536) return false;
+  if (method == 0) {  // multiply-accumulate counts of the two options
+    const double o1 = (double)T * d * d + (double)n * T * d;
+    const double o2 = (double)n * H * T * d + (double)n * d * d;
+    method = o1 < o2 ? 1 : 2;
+  }
+  if (method == 1 && !w_bf16) return false;  // V = K.W_KV is formed by the bf16 MFMA product
+  p->method = method;
+  p->qw = n > 64 ? 4 : (n > 32 ? 2 : 1);
+  const long long nqg = (n + 32LL * p->qw - 1) / (32LL * p->qw);
+  const long long ncb = method == 2 ? (d + 127) / 128 : 1;
+  const long long wgs = ncb * H * nqg;
+  int nsplit = 1;
+  if (method == 2) {  // split the context while the grid is below two workgroups per compute unit
+    while (wgs * nsplit * 2 <= 2LL * ncu && (long long)nsplit * 2 * kMTile * 4 <= T) nsplit *= 2;
+  }
+  p->nsplit = nsplit;
+  p->Ts = ((T + nsplit - 1) / nsplit + kMTile - 1) / kMTile * kMTile;
+  p->nsplit = (T + p->Ts - 1) / p->Ts;
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off += (b + 255) & ~(size_t)255;
+    return o;
+  };
+  p->fin = DecodePlan{};
+  if (method == 2) {
+    p->fin.nslots = n * p->nsplit;
+    const int big = proj_rows(dh, true);
+    const long long grid = (long long)H * ((d + big - 1) / big) * ((n + 7) / 8);
+    p->fin.proj_rows = grid * 2 >= ncu ? big : proj_rows(dh, false);
+    p->fin.npc = (int)((d + p->fin.proj_rows - 1) / p->fin.proj_rows);
+    p->fin.nch = 1;
+    p->fin.off_U = take((size_t)H * p->fin.nslots * d * sizeof(float));
+    p->fin.off_ml = take((size_t)p->fin.nslots * 2 * H * sizeof(float));
+    p->fin.off_op = take((size_t)p->fin.npc * n * H * dh * sizeof(float));
+    p->off_v = 0;
+  } else {
+    p->off_v = take((size_t)T * d * sizeof(uint16_t));
+  }
+  p->bytes = off;
+  return true;
+}
+
+hipError_t launch_multi(const MultiPlan& pl, const float* Q, const void* K, const int32_t* limits,
+                        const void* W, bool w_bf16, float* out, int n, int H, int dh, int T, float scale,
+                        char* ws, hipStream_t s) {
+  const int d = H * dh;
+  MultiParams mp{};
+  mp.Q = Q;
+  mp.K = static_cast<const uint16_t*>(K);
+  mp.limits = limits;
+  mp.n = n;
+  mp.H = H;
+  mp.d = d;
+  mp.T = T;
+  mp.nsplit = pl.nsplit;
+  mp.Ts = pl.Ts;
+  mp.qscale = scale * kLog2e;
+  hipError_t e;
+  if (pl.method == 1) {
+    uint16_t* V = reinterpret_cast<uint16_t*>(ws + pl.off_v);
+    e = launch_prefill_bf16(K, W, V, 1, T, d, T, nullptr, s);  // V = K . W_KV, rounded to bf16
+    if (e != hipSuccess) return e;
+    mp.Vs = V;
+    mp.out = out;
+    return dh == 64 ? launch_mq_qw<64, 1>(pl, mp, s) : launch_mq_qw<128, 1>(pl, mp, s);
+  }
+  mp.Vs = mp.K;
+  mp.U = reinterpret_cast<float*>(ws + pl.fin.off_U);
+  mp.ml = reinterpret_cast<float*>(ws + pl.fin.off_ml);
+  mp.nslots = pl.fin.nslots;
+  e = dh == 64 ? launch_mq_qw<64, 2>(pl, mp, s) : launch_mq_qw<128, 2>(pl, mp, s);
+  if (e != hipSuccess) return e;
+  DecodeArgs a{};
+  a.q = Q;
+  a.K = K;
+  a.lengths = nullptr;
+  a.W = W;
+  a.out = out;
+  a.B = n;
+  a.H = H;
+  a.dh = dh;
+  a.d = d;
+  a.T_max = T;
+  a.nslots = pl.fin.nslots;
+  a.scale = scale;
+  a.w_bf16 = w_bf16;
+  a.ws = ws;
+  return launch_finish_fixed(pl.fin, a, pl.nsplit, s);
+}
+
+}  // namespace slim
