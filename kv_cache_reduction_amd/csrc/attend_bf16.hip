@@ -32,10 +32,9 @@
 //    of step i with the registers it read one iteration earlier.  The
 //    independent halves fill each other's latency.
 //  * Online softmax: lane l handles head l%32, tokens 4*(l/32)..+3 (the MFMA
-//    A-operand layout); weights are rounded to bf16 and one 32x32x16 bf16
-//    MFMA per 32 output columns takes the step's 8 tokens in the low half of
-//    its K dimension; B operands come from byte permutes (a 4x8 -> 8x4
-//    transpose of 16-bit values in registers).
+//    A-operand layout); weights are rounded to bf16 and one 32x32x8 bf16
+//    MFMA per 32 output columns takes the step's 8 tokens; its B operand
+//    comes from one transpose read (ds_read_b64_tr_b16) of the ring slot.
 //  * Lazy rescaling: each head keeps a reference max m (log2 units) and the
 //    accumulator holds sum_t 2^(s_t - m) K[t]; m only moves (and the
 //    accumulator rows are rescaled) when a score exceeds it by more than 8,
