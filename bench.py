@@ -156,6 +156,107 @@ def time_step(wl, torch, slim, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def _event_ms(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def _graph_ms(torch, fn, out, steps):
+    """Device time of one call: the call captured once in a graph and
+    replayed `steps` times between events (a call of a few tens of us is
+    otherwise bound by the host's launch rate).  Every replay's output must
+    equal the eager call's bit for bit."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay differs from the eager call")
+    E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def multi_query_flops(n, H, dh, T, limits, option):
+    """Algorithmic flops of n queries over one context: scores 2 L d, the
+    softmax times K on all d columns per head 2 H L d and the projection
+    2 n d^2 (option 2), or V = K.W_KV 2 T d^2 and the softmax times V 2 L d
+    (option 1), with L the summed rows the queries attend."""
+    d = H * dh
+    L = float(np.sum(np.clip(limits, 0, T))) if limits is not None else float(n) * T
+    if option == 1:
+        return 2.0 * T * d * d + 2.0 * L * d + 2.0 * L * d
+    return 2.0 * L * d + 2.0 * H * L * d + 2.0 * n * d * d
+
+
+def time_multi(torch, slim, steps):
+    """Many queries over one context: Whisper-large-shaped cross-attention of
+    64 decoder queries over one shared encoder context (T=1500, d=1280), and
+    a GPT-2-small-shaped prompt of 2048 tokens attending causally over itself
+    (d=768).  K written by slim_prefill from bf16 X and W_K; bf16 W_KV.
+    Device time per call by graph replay."""
+    import synthetic as syn
+    out = {}
+    cases = [("shared_context", syn.CONFIGS["c4"], 64, False), ("prompt", syn.CONFIGS["c1"], 2048, True)]
+    for name, cfg, n, causal in cases:
+        w = syn.weights(cfg)
+        T = cfg.T_max
+        one = syn.shrink(cfg, B=1)
+        Xb = syn.f32_to_bf16_bits(syn.x_rows(one, 0, 0, T))
+        K = torch.zeros((1, T, cfg.d), dtype=torch.bfloat16, device="cuda")
+        slim.prefill(bf16_dev(Xb)[None], bf16_dev(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))), K)
+        K = K[0]
+        Wkv = bf16_dev(slim.wkv(syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))).astype(
+            np.float64), w.W_V, "bf16"))
+        if causal:
+            X = syn.x_rows(one, 0, T - n, T).astype(np.float64)
+            Q = torch.from_numpy((X @ w.W_Q).astype(np.float32)).cuda()
+            lim_np = (T - n) + np.arange(n, dtype=np.int32) + 1
+            lim = torch.from_numpy(lim_np).cuda()
+        else:
+            Q = torch.from_numpy(syn.queries(cfg, w)[:n]).cuda()
+            lim_np, lim = None, None
+        o = torch.empty((n, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+        rec = {"workload": (f"{n} queries over one context of {T} rows, d={cfg.d} H={cfg.H} dh={cfg.dh}"
+                            + (", causal (prompt phase)" if causal else ", shared (cross-attention)")),
+               "auto_option": slim.multi_query_option(n, cfg.H, cfg.dh, T)}
+        for opt in (1, 2):
+            ws = slim.workspace(slim.multi_query_workspace_bytes(n, cfg.H, cfg.dh, T, torch.bfloat16, opt))
+            ms = _graph_ms(torch, lambda: slim.multi_query(Q, K, Wkv, o, cfg.H, cfg.dh, limits=lim,
+                                                           scale=cfg.scale, option=opt, ws=ws), o, steps)
+            fl = multi_query_flops(n, cfg.H, cfg.dh, T, lim_np, opt)
+            rec[f"option{opt}"] = {"us": ms * 1e3, "tokens_s": n / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
+                                   "mfma_bf16_frac": fl / (ms * 1e-3) / 2.5e15}
+            log(f"[bench] {name}: option {opt}: {ms * 1e3:.1f} us, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        out[name] = rec
+    return out
+
+
 def time_kv(wl, torch, slim, steps, warmup):
     cfg = wl.cfg
     args = lambda i: (wl.q, wl.K[i % len(wl.K)], wl.V[i % len(wl.V)], wl.ld, wl.out, cfg.H, cfg.dh,
@@ -343,6 +444,7 @@ def main():
             "projection_weight_bytes": wbytes}
         log(f"[bench] generation step: {ms_gen * 1e3:.1f} us/step "
             f"({(ms_gen - ms_step) * 1e3:.1f} us over the decode)")
+        res["multi_query"] = time_multi(torch, slim, max(10, args.steps // 2))
         ms_kv = time_kv(wl, torch, slim, max(10, args.steps // 2), 3)
         res["comparator"] = {"what": "standard MHA decode over explicit bf16 K and V caches (same box)",
                              "tokens_s": cfg.B / (ms_kv * 1e-3), "ms_per_step": ms_kv,

@@ -29,8 +29,9 @@
 //    (ds_read_b64_tr_b16) of the tile rows.
 //  * Option 2 writes unnormalised partial rows U[h, q*nsplit + split, cols]
 //    and (column block 0) m and the normaliser l, the layout the decode
-//    finish merges and projects by W_KV.  Option 1 (one split) writes the
-//    normalised output rows directly.
+//    finish merges and projects by W_KV.  Option 1 writes the normalised
+//    output rows directly (one split) or partial rows of the head's dh
+//    columns that multi_merge combines.
 #include "common.hpp"
 #include "internal.hpp"
 #include "multi.hpp"
@@ -275,6 +276,20 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
       mls[h] = m_ref;
       mls[p.H + h] = l_row;
     }
+  } else if (p.nsplit > 1) {  // option 1 over context splits: partial rows [h][slot][DH], m, l
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * hh + (i & 3), qq = qbase + r;
+      if (qq >= p.n) continue;
+      float* dst = p.U + ((size_t)h * p.nslots + (size_t)qq * p.nsplit + split) * DH;
+#pragma unroll
+      for (int s = 0; s < S::NCT; ++s) dst[32 * s + m] = acc[s][i];
+    }
+    if (hh == 0 && qok) {
+      float* mls = p.ml + (size_t)(q * p.nsplit + split) * 2 * p.H;
+      mls[h] = m_ref;
+      mls[p.H + h] = l_row;
+    }
   } else {
     __syncthreads();  // rv is reused for the normalisers
     if (hh == 0) rv[m] = l_row;
@@ -290,6 +305,30 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
       for (int s = 0; s < S::NCT; ++s) dst[32 * s + m] = acc[s][i] * inv;
     }
   }
+}
+
+// Option 1 over context splits: out[q, h, j] = sum_s 2^(m_s - m*) U_s[h, j] /
+// sum_s 2^(m_s - m*) l_s (log-sum-exp merge of the splits), zero for a query
+// with no rows.
+__global__ void __launch_bounds__(256) multi_merge_kernel(const float* __restrict__ U,
+                                                          const float* __restrict__ ml,
+                                                          float* __restrict__ out, int n, int H, int dh,
+                                                          int ns, int nslots) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)n * H * dh) return;
+  const int j = (int)(i % dh), h = (int)((i / dh) % H), q = (int)(i / ((long long)dh * H));
+  float mx = kNegInf;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[(size_t)(q * ns + s) * 2 * H + h]);
+  float num = 0.f, den = 0.f;
+  if (mx > kNegInf) {
+    for (int s = 0; s < ns; ++s) {
+      const float* mls = ml + (size_t)(q * ns + s) * 2 * H;
+      const float w = fast_exp2(mls[h] - mx);
+      den = fmaf(w, mls[H + h], den);
+      num = fmaf(w, U[((size_t)h * nslots + (size_t)q * ns + s) * dh + j], num);
+    }
+  }
+  out[i] = den > 0.f ? num / den : 0.f;
 }
 
 template <int DH, int QW, int OPT>
@@ -332,10 +371,9 @@ bool make_multi_plan(int n, int H, int dh, int T, int method, bool w_bf16, int n
   const long long nqg = (n + 32LL * p->qw - 1) / (32LL * p->qw);
   const long long ncb = method == 2 ? (d + 127) / 128 : 1;
   const long long wgs = ncb * H * nqg;
+  // split the context while the grid is below two workgroups per compute unit
   int nsplit = 1;
-  if (method == 2) {  // split the context while the grid is below two workgroups per compute unit
-    while (wgs * nsplit * 2 <= 2LL * ncu && (long long)nsplit * 2 * kMTile * 4 <= T) nsplit *= 2;
-  }
+  while (wgs * nsplit * 2 <= 2LL * ncu && (long long)nsplit * 2 * kMTile * 4 <= T) nsplit *= 2;
   p->nsplit = nsplit;
   p->Ts = ((T + nsplit - 1) / nsplit + kMTile - 1) / kMTile * kMTile;
   p->nsplit = (T + p->Ts - 1) / p->Ts;
@@ -359,6 +397,11 @@ bool make_multi_plan(int n, int H, int dh, int T, int method, bool w_bf16, int n
     p->off_v = 0;
   } else {
     p->off_v = take((size_t)T * d * sizeof(uint16_t));
+    if (p->nsplit > 1) {
+      p->fin.nslots = n * p->nsplit;
+      p->fin.off_U = take((size_t)H * p->fin.nslots * dh * sizeof(float));
+      p->fin.off_ml = take((size_t)p->fin.nslots * 2 * H * sizeof(float));
+    }
   }
   p->bytes = off;
   return true;
@@ -386,7 +429,17 @@ hipError_t launch_multi(const MultiPlan& pl, const float* Q, const void* K, cons
     if (e != hipSuccess) return e;
     mp.Vs = V;
     mp.out = out;
-    return dh == 64 ? launch_mq_qw<64, 1>(pl, mp, s) : launch_mq_qw<128, 1>(pl, mp, s);
+    if (pl.nsplit > 1) {
+      mp.U = reinterpret_cast<float*>(ws + pl.fin.off_U);
+      mp.ml = reinterpret_cast<float*>(ws + pl.fin.off_ml);
+      mp.nslots = pl.fin.nslots;
+    }
+    e = dh == 64 ? launch_mq_qw<64, 1>(pl, mp, s) : launch_mq_qw<128, 1>(pl, mp, s);
+    if (e != hipSuccess || pl.nsplit == 1) return e;
+    const long long tot = (long long)n * H * dh;
+    hipLaunchKernelGGL(multi_merge_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s,
+                       (const float*)mp.U, (const float*)mp.ml, out, n, H, dh, pl.nsplit, pl.fin.nslots);
+    return hipGetLastError();
   }
   mp.Vs = mp.K;
   mp.U = reinterpret_cast<float*>(ws + pl.fin.off_U);

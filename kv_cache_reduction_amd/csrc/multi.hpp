@@ -8,9 +8,9 @@ namespace slim {
 struct MultiPlan {
   int method;      // 1: V = K.W_KV formed, then softmax . V; 2: softmax . K, then W_KV
   int qw;          // waves (32 queries each) per workgroup
-  int nsplit, Ts;  // context splits of Ts rows (option 2)
+  int nsplit, Ts;  // context splits of Ts rows
   size_t off_v;    // option 1: [T, d] bf16 values
-  DecodePlan fin;  // option 2: partial rows and the merge / projection (offsets, row blocks)
+  DecodePlan fin;  // partial rows (option 2; option 1 with splits) and the merge / projection
   size_t bytes;
 };
 

@@ -5,94 +5,124 @@
 //
 // bf16: M = B*n rows, N = d, K = d on v_mfma_f32_32x32x8_bf16, fp32
 // accumulation, round-to-nearest-even bf16 output.  Workgroup tile 128x128
-// (four waves of 64x64, 2x2 MFMA tiles each), K-step 32 through LDS.  A is
-// stored row-major [m][k]; B is stored transposed [n][k] so both MFMA
-// operands are one 8-byte LDS read per lane.
+// (four waves of 64x64, 2x2 MFMA tiles each; 64x128 with waves of 32x64
+// when the 128-row grid would leave compute units idle), 64-deep k blocks.  Both
+// operands sit in LDS in their natural row-major layouts: a lane's A
+// fragment (4 consecutive k of one row) is one 8-byte read; its B fragment
+// (4 consecutive k of one column) is one transpose read (ds_read_b64_tr_b16)
+// of four W rows.  The next k block is loaded into registers while the
+// current one is multiplied.
 // fp32: a plain LDS-tiled VALU GEMM (64x64 tiles, 4x4 outputs per thread).
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace slim {
 
-constexpr int kPM = 128, kPN = 128, kPK = 32, kPKpad = kPK + 4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_p;
 
+constexpr int kPN = 128, kPK = 64;
+constexpr int kAPitch = kPK * 2 + 8;   // bytes per A row in LDS (rows 8 bytes apart in bank order)
+constexpr int kBPitch = kPN * 2 + 16;  // bytes per W row in LDS
+
+template <int PM>  // rows per workgroup: 128, or 64 when the 128-row grid would leave compute units idle
 __global__ void __launch_bounds__(256) prefill_bf16_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ W,
                                                            uint16_t* __restrict__ Kc, int B, int n,
                                                            int d, int T_max,
                                                            const int32_t* __restrict__ t0) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kPM * kPKpad];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kPN * kPKpad];
+  constexpr int MI = PM / 64;  // 32-row MFMA tiles per wave (waves 2 x 2, each PM/2 x 64)
+  constexpr int AC = PM / 32;  // 16-byte A chunks per thread and k block
+  __shared__ __attribute__((aligned(16))) char As[PM * kAPitch];
+  __shared__ __attribute__((aligned(16))) char Bs[kPK * kBPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int M = B * n;
-  const int m0 = blockIdx.y * kPM, n0 = blockIdx.x * kPN;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
+  const long long M = (long long)B * n;
+  const long long m0 = (long long)blockIdx.y * PM;
+  const int n0 = blockIdx.x * kPN;
 
-  f32x16 acc[2][2];
+  // staging: AC chunks of A (row c/8, k 8*(c%8)) and 4 of W (row c/16, col 8*(c%16))
+  uint4 sa[AC], sb[4];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i;
+      const int ar = c >> 3, ak = (c & 7) * 8;
+      sa[i] = make_uint4(0, 0, 0, 0);
+      if (m0 + ar < M && k0 + ak < d) sa[i] = *reinterpret_cast<const uint4*>(X + (size_t)(m0 + ar) * d + k0 + ak);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int br = c >> 4, bc = (c & 15) * 8;
+      sb[i] = make_uint4(0, 0, 0, 0);
+      if (k0 + br < d && n0 + bc < d) sb[i] = *reinterpret_cast<const uint4*>(W + (size_t)(k0 + br) * d + n0 + bc);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i;
+      const int ar = c >> 3, ak = (c & 7) * 8;
+      char* pa = As + ar * kAPitch + ak * 2;
+      *reinterpret_cast<uint2*>(pa) = make_uint2(sa[i].x, sa[i].y);
+      *reinterpret_cast<uint2*>(pa + 8) = make_uint2(sa[i].z, sa[i].w);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int br = c >> 4, bc = (c & 15) * 8;
+      *reinterpret_cast<uint4*>(Bs + br * kBPitch + bc * 2) = sb[i];
+    }
+  };
+
+  f32x16 acc[MI][2];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0};
 
+  // A fragment: row wm*PM/2 + 32i + lane%32, k 8*kk + 4*h .. +3
+  const char* a_base = As + (wm * (PM / 2) + (lane & 31)) * kAPitch + h * 8;
+  // B fragment by transpose read: lane L points at columns
+  // 16*((L/16)%2) + 4*(L%4) of W row 4*(L/32) + (L%16)/4 (within a 32-column
+  // tile and an 8-row k step); lane l ends with column l%32 of rows 4*(l/32)..+3
+  const uint32_t b_base = (uint32_t)(uintptr_t)Bs + (uint32_t)((4 * h + ((lane & 15) >> 2)) * kBPitch +
+                                                               (wn * 64 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+
+  load(0);
   for (int k0 = 0; k0 < d; k0 += kPK) {
-    // A tile: 128 rows x 32 k, 16-byte chunks
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int ch = tid + r * 256;
-      const int row = ch >> 2, kc = (ch & 3) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + row < M && k0 + kc < d) v = *reinterpret_cast<const uint4*>(X + (size_t)(m0 + row) * d + k0 + kc);
-      uint2* dst = reinterpret_cast<uint2*>(As + row * kPKpad + kc);
-      dst[0] = make_uint2(v.x, v.y);
-      dst[1] = make_uint2(v.z, v.w);
-    }
-    // B tile: 32 k x 128 n from W[k][n], stored transposed [n][k]
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int ch = tid + r * 256;
-      const int kr = ch >> 4, nc = (ch & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + kr < d && n0 + nc < d) v = *reinterpret_cast<const uint4*>(W + (size_t)(k0 + kr) * d + n0 + nc);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        Bs[(nc + i) * kPKpad + kr] = (uint16_t)((i & 1) ? (w4[i >> 1] >> 16) : (w4[i >> 1] & 0xffffu));
-    }
+    store();
     __syncthreads();
+    if (k0 + kPK < d) load(k0 + kPK);
 #pragma unroll
-    for (int kk = 0; kk < kPK; kk += 8) {
-      const int kq = kk + 4 * (lane >> 5);
-      s16x4 a[2], bv[2];
+    for (int kk = 0; kk < kPK / 8; ++kk) {
+      s16x4 a[MI], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const s16x4*>(As + row * kPKpad + kq);
-      }
+      for (int i = 0; i < MI; ++i) a[i] = *reinterpret_cast<const s16x4*>(a_base + 32 * i * kAPitch + 16 * kk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = wn * 64 + j * 32 + (lane & 31);
-        bv[j] = *reinterpret_cast<const s16x4*>(Bs + col * kPKpad + kq);
-      }
+      for (int j = 0; j < 2; ++j)
+        b[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_p*)(size_t)(b_base + (uint32_t)(8 * kk * kBPitch + 64 * j)));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a[i], bv[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + j * 32 + (lane & 31);
       if (col >= d) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const long long m = m0 + wm * (PM / 2) + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m >= M) continue;
-        const int b = m / n, r = m - b * n;
+        const int b = (int)(m / n), r = (int)(m - (long long)b * n);
         const int t = (t0 ? t0[b] : 0) + r;
         if (t < 0 || t >= T_max) continue;
         Kc[((size_t)b * T_max + t) * d + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
@@ -144,9 +174,17 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(const float* __restric
 hipError_t launch_prefill_bf16(const void* X, const void* W, void* Kc, int B, int n, int d,
                                int T_max, const int32_t* t0, hipStream_t s) {
   const long long M = (long long)B * n;
-  dim3 grid((d + kPN - 1) / kPN, (unsigned)((M + kPM - 1) / kPM));
-  hipLaunchKernelGGL(prefill_bf16_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(X),
-                     static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Kc), B, n, d, T_max, t0);
+  const unsigned gx = (unsigned)((d + kPN - 1) / kPN);
+  const long long g128 = (M + 127) / 128;
+  if (g128 * gx >= 512 || g128 > 65535) {
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(gx, (unsigned)g128), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W),
+                       static_cast<uint16_t*>(Kc), B, n, d, T_max, t0);
+  } else {
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(gx, (unsigned)((M + 63) / 64)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W),
+                       static_cast<uint16_t*>(Kc), B, n, d, T_max, t0);
+  }
   return hipGetLastError();
 }
 
