@@ -107,25 +107,31 @@ class Workload:
 
 
 def time_slim(wl, torch, slim, steps, warmup):
+    """Step time: `steps` slim_decode calls back to back between two events.
+    Attend time (for the roofline): a second loop with an event pair around
+    each attend launch; those events sit between kernels, so this loop is
+    not used for the step time."""
     cfg = wl.cfg
     args = lambda i: (wl.q, wl.K[i % len(wl.K)], wl.ld, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, wl.ws)
     for i in range(warmup):
         slim.decode(*args(i))
     torch.cuda.synchronize()
     E = torch.cuda.Event
+    start, stop = E(enable_timing=True), E(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        slim.decode(*args(i))
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
     a0 = [E(enable_timing=True) for _ in range(steps)]
     a1 = [E(enable_timing=True) for _ in range(steps)]
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
     for i in range(steps):
         a0[i].record()
         slim.decode_attend(*args(i))
         a1[i].record()
         slim.decode_finish(*args(i))
-    stop.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / steps
     attend = np.array([a0[i].elapsed_time(a1[i]) for i in range(steps)])
     return ms_step, attend
 

@@ -26,6 +26,7 @@
 namespace slim {
 
 constexpr int kSeqPerProj = 8;  // sequences per workgroup
+constexpr int kMergeBatch = 4;  // slots whose loads a thread issues together
 
 template <int DH, bool WBF16, int PR>
 __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __restrict__ lengths,
@@ -58,29 +59,29 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * kSeqPerProj;
   const int nr = min(PR, d - r0), nb = min(kSeqPerProj, B - b0);
 
-  // W_KV rows [r0, r0 + PR) of head h's columns, in registers
+  // W_KV rows [r0, r0 + PR) of head h's columns, in registers.  The loads
+  // are unconditional (rows past the block clamped, then zeroed) so that
+  // they are all in flight together.
   const int jq = tid % JQ, rs = tid / JQ;
   float w[RPT][JW];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rs * RPT + i;
-    const size_t base = (size_t)(r0 + r) * d + (size_t)h * DH + jq * JW;
-    if (r < nr) {
-      if constexpr (WBF16 && JW == 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + base);
-        w[i][0] = bf_lo(v.x); w[i][1] = bf_hi(v.x); w[i][2] = bf_lo(v.y); w[i][3] = bf_hi(v.y);
-        w[i][4] = bf_lo(v.z); w[i][5] = bf_hi(v.z); w[i][6] = bf_lo(v.w); w[i][7] = bf_hi(v.w);
-      } else {
-#pragma unroll
-        for (int k = 0; k < JW; ++k) {
-          if (WBF16) w[i][k] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(W)[base + k] << 16);
-          else w[i][k] = static_cast<const float*>(W)[base + k];
-        }
-      }
+    const bool live = r < nr;
+    const size_t base = (size_t)(r0 + (live ? r : nr - 1)) * d + (size_t)h * DH + jq * JW;
+    if constexpr (WBF16 && JW == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + base);
+      w[i][0] = bf_lo(v.x); w[i][1] = bf_hi(v.x); w[i][2] = bf_lo(v.y); w[i][3] = bf_hi(v.y);
+      w[i][4] = bf_lo(v.z); w[i][5] = bf_hi(v.z); w[i][6] = bf_lo(v.w); w[i][7] = bf_hi(v.w);
     } else {
 #pragma unroll
-      for (int k = 0; k < JW; ++k) w[i][k] = 0.f;
+      for (int k = 0; k < JW; ++k) {
+        if (WBF16) w[i][k] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(W)[base + k] << 16);
+        else w[i][k] = static_cast<const float*>(W)[base + k];
+      }
     }
+#pragma unroll
+    for (int k = 0; k < JW; ++k) w[i][k] = live ? w[i][k] : 0.f;
   }
 
   // slots of sequence b: the chunks its rows fall in (decode), or a fixed
@@ -119,11 +120,11 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
       const bool cols = 4 * c4 < nr;
       const float* src = U + ((size_t)h * nslots + slot0) * d + r0 + 4 * c4;
       const float* mls = ml + (size_t)slot0 * 2 * H + h;
-      for (int i = ss; i < ns; i += 4 * nss) {  // four slots per round, loads first
-        float4 x[4];
-        float ms[4], ls[4];
+      for (int i = ss; i < ns; i += kMergeBatch * nss) {  // a batch of slots per round, loads first
+        float4 x[kMergeBatch];
+        float ms[kMergeBatch], ls[kMergeBatch];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kMergeBatch; ++k) {
           const int j = i + k * nss;
           const bool ok = j < ns;
           ms[k] = ok ? mls[(size_t)j * 2 * H] : kNegInf;
@@ -142,8 +143,10 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
           }
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) bad |= ms[k] != ms[k];  // an attend piece marked NaN
-        const float mn = fmaxf(fmaxf(m, fmaxf(ms[0], ms[1])), fmaxf(ms[2], ms[3]));
+        for (int k = 0; k < kMergeBatch; ++k) bad |= ms[k] != ms[k];  // an attend piece marked NaN
+        float mn = m;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) mn = fmaxf(mn, ms[k]);
         if (mn > kNegInf) {
           const float sc = fast_exp2(m - mn);
           acc.x *= sc;
@@ -152,7 +155,7 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
           acc.w *= sc;
           l *= sc;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < kMergeBatch; ++k) {
             const float q = fast_exp2(ms[k] - mn);
             l = fmaf(q, ls[k], l);
             acc.x = fmaf(q, x[k].x, acc.x);
@@ -224,8 +227,13 @@ __global__ void __launch_bounds__(256) proj_reduce_kernel(const float* __restric
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < npc; ++k) s += part[(size_t)k * n + i];
+  for (int k0 = 0; k0 < npc; k0 += 16) {  // a batch's loads first, then the sum in order
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = k0 + j < npc ? part[(size_t)(k0 + j) * n + i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
   out[i] = s;
 }
 
