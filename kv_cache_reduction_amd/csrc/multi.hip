@@ -11,17 +11,17 @@
 //    buffered, one barrier per tile): head h's DH key columns for the scores
 //    and the value block: 128 columns of K (option 2) or head h's DH columns
 //    of V (option 1).  All waves of the workgroup share the tile.
-//  * Scores S = Q_h . K_h^T on 32x32x8 bf16 MFMA with Q split into bf16 high
-//    and low parts (two MFMAs per step), so the products keep about 16 bits
-//    of Q; fp32 accumulation.  The reduction over the head's DH dimensions is
-//    ordered so that a lane's B operand is one 8-byte LDS read of its row:
-//    lanes 0-31 take dimensions [0, DH/2), lanes 32-63 [DH/2, DH), four per
-//    step, and the A operand (Q, in registers for the whole kernel) follows
-//    the same order.
-//  * The 32x32 score tile goes through a private LDS buffer from the MFMA
-//    result layout (lane = context row) to the A-operand layout (lane =
-//    query, 16 rows each, halves joined by a lane swap), where the online
-//    softmax runs: rows past a query's limit are -inf; lazy rescaling keeps
+//  * Scores on 32x32x8 bf16 MFMA, computed transposed (S^T = K_h . Q_h^T,
+//    the tile's K rows as the A operand, Q as the B operand) with Q split
+//    into bf16 high and low parts (two MFMAs per step), so the products keep
+//    about 16 bits of Q; fp32 accumulation.  The reduction over the head's
+//    DH dimensions is ordered so that a lane's A operand is one 8-byte LDS
+//    read of its row: lanes 0-31 take dimensions [0, DH/2), lanes 32-63
+//    [DH/2, DH), four per step, and Q (in registers for the whole kernel)
+//    follows the same order.
+//  * The transposed result already has the A-operand layout of P . V (lane =
+//    query, 16 context rows each, halves joined by a lane swap), where the
+//    online softmax runs: rows past a query's limit are -inf; lazy rescaling keeps
 //    a reference max m (log2 units; Q is pre-scaled by scale*log2 e) that
 //    moves only when a score exceeds it by more than 8, so weights stay
 //    below 2^8; the accumulator rows are then rescaled through LDS.
@@ -42,7 +42,6 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_m;
 
 constexpr int kMTile = 32;              // context rows per tile
 constexpr float kMultiSlack = 8.f;      // log2 units
-constexpr int kSPitch = 33;             // floats per row of the private score buffer
 
 struct MultiParams {
   const float* Q;          // [n, d]
@@ -85,8 +84,7 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   constexpr int CPT = (S::SCH + S::VCH + NT - 1) / NT;  // chunks per thread and tile
   extern __shared__ __attribute__((aligned(16))) char msm[];
   char* tiles = msm;                                               // [2][TILE]
-  float* sbuf = reinterpret_cast<float*>(msm + 2 * S::TILE);       // [QW][32][kSPitch]
-  float* rowv = sbuf + QW * 32 * kSPitch;                          // [QW][32]
+  float* rowv = reinterpret_cast<float*>(msm + 2 * S::TILE);       // [QW][32]
   int* lim_max = reinterpret_cast<int*>(rowv + QW * 32);           // [1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, m = lane & 31;
@@ -166,7 +164,6 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     }
   };
 
-  float* sb = sbuf + wave * 32 * kSPitch;
   float* rv = rowv + wave * 32;
   // transpose-read offset of the value part: lane L reads 4 columns
   // 32s + 16*((L/16)%2) + 4*(L%4) of row 8k + 4*(L/32) + (L%16)/4; the
@@ -188,28 +185,27 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     const int tb = t_begin + it * kMTile;
     if (it + 1 < ntiles) load_tile(tb + kMTile);
 
-    // scores of the tile (MFMA result layout: lane = row m of column l%32)
+    // scores of the tile, transposed: S^T = K_h . Q_h^T with the K rows as
+    // the A operand and Q (registers) as the B operand.  The result layout
+    // leaves lane l with query l%32 at context rows 8k + 4*hh + j (register
+    // 4k + j), which is exactly the A-operand layout of P . V below.
     f32x16 sc = f32x16{0};
     {
-      const char* srow = buf + m * S::SP + hh * DH;  // this lane's context row, its half
+      const char* srow = buf + m * S::SP + hh * DH;  // context row l%32, this half's dimensions
 #pragma unroll
       for (int k = 0; k < DH / 8; ++k) {
-        const s16x4 b = *reinterpret_cast<const s16x4*>(srow + 8 * k);
-        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(qh[k], b, sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ql[k], b, sc, 0, 0, 0);
+        const s16x4 a = *reinterpret_cast<const s16x4*>(srow + 8 * k);
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, qh[k], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, ql[k], sc, 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sb[(8 * (i >> 2) + 4 * hh + (i & 3)) * kSPitch + m] = sc[i];
-    // A-operand layout: row m, context rows 8k + 4*hh + j
     float v[4][4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 8 * k + 4 * hh + j;
-        const float x = sb[m * kSPitch + t];
-        v[k][j] = (tb + t < min(lim, t_end)) ? x : kNegInf;
+        v[k][j] = (tb + t < min(lim, t_end)) ? sc[4 * k + j] : kNegInf;
       }
     float mx = kNegInf;
 #pragma unroll
@@ -334,7 +330,7 @@ __global__ void __launch_bounds__(256) multi_merge_kernel(const float* __restric
 template <int DH, int QW, int OPT>
 static hipError_t launch_mq(const MultiPlan& pl, const MultiParams& mp, hipStream_t s) {
   using S = MultiShape<DH, OPT>;
-  const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * kSPitch * 4 + (size_t)QW * 32 * 4 + 16;
+  const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * 4 + 16;
   auto kern = multi_attend_kernel<DH, QW, OPT>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -129,3 +129,27 @@ def test_rejects_bad_arguments():
     out2 = torch.empty((4, 4, 32), dtype=torch.float32, device="cuda")
     with pytest.raises(slim.SlimError):      # dh = 32 is not built
         slim.multi_query(Q, K, W, out2, 4, 32, option=2)
+
+
+@pytest.mark.parametrize("T,n,option", [(1, 1, 1), (1, 5, 2), (33, 1, 1), (33, 70, 2), (95, 130, 0)])
+def test_small_contexts_and_query_counts(T, n, option):
+    """Contexts shorter than one tile, a single query, query counts that
+    leave partial query blocks, in both options."""
+    cfg = syn.shrink(syn.CONFIGS["c4"], B=n, T_max=T, len_lo=T, len_hi=T)
+    w, K, Wkv = _context(cfg, T)
+    Q = syn.queries(cfg, w)
+    _run(f"small T={T} n={n}", cfg, Q, K, Wkv, w, None, option)
+
+
+def test_all_limits_zero_gives_zeros():
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=9, T_max=40, len_lo=40, len_hi=40)
+    w, K, Wkv = _context(cfg, 40)
+    Q = syn.queries(cfg, w)
+    for option in (1, 2):
+        import torch
+        import kv_cache_reduction_amd as slim
+        out = torch.full((9, cfg.H, cfg.dh), 7.0, dtype=torch.float32, device="cuda")
+        slim.multi_query(to_dev(Q), to_dev(K), Wkv, out, cfg.H, cfg.dh,
+                         limits=to_dev(np.zeros(9, dtype=np.int32)), scale=cfg.scale, option=option)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0

@@ -197,3 +197,11 @@ def test_step_c3_full_size_sampled_heads():
     assert err <= TOL["bf16"]
     got = bf16_bits(Kd[:, T - 1])
     check_prefill_bf16(got, x.astype(np.float64), WK64, "c3 appended row")
+
+
+def test_step_one_row_cache_and_many_sequences():
+    """T_max = 1 (the first step fills the cache, the next finds it full) and
+    B = 100 (seven projection groups of 16 sequences, a ragged last one)."""
+    cfg = syn.shrink(syn.CONFIGS["c1"], B=100, T_max=1, len_lo=0, len_hi=1)
+    lens = (np.arange(100) % 2).astype(np.int32)        # empty and full caches
+    _run_case("T_max=1 B=100", cfg, lens)
