@@ -151,3 +151,55 @@ def test_wkv_bad_args(slim):
     a = np.eye(4)
     out = np.empty((4, 4), np.float32)
     assert slim.lib.slim_wkv(a.ctypes.data, a.ctypes.data, 4, out.ctypes.data, 5) == 2
+
+
+def test_step_rejects_bad_arguments(slim):
+    f = slim.lib.slim_step
+    ok = dict(x=16, WQ=16, WK=16, wdt=slim.BF16, K=16, kdt=slim.BF16, lens=4, nxt=8, W=16, wkv=slim.BF16,
+              out=4, B=1, H=32, dh=128, T=1024, scale=0.088, ws=256, wsb=1 << 30, stream=None)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return f(a["x"], a["WQ"], a["WK"], a["wdt"], a["K"], a["kdt"], a["lens"], a["nxt"], a["W"], a["wkv"],
+                 a["out"], a["B"], a["H"], a["dh"], a["T"], a["scale"], a["ws"], a["wsb"], a["stream"])
+    for field in ("x", "WQ", "WK", "nxt", "K", "lens", "W", "out", "ws"):
+        assert call(**{field: None}) == 1, field
+    assert call(nxt=4) == 1                     # lengths_next aliases lengths
+    assert call(WQ=24) == 1                     # W_Q not 16-byte aligned
+    assert call(wdt=5) == 2
+    assert call(B=0) == 1
+    assert call(scale=float("inf")) == 1
+
+
+def test_multi_query_rejects_bad_arguments(slim):
+    f = slim.lib.slim_multi_query
+    ok = dict(Q=16, K=16, kdt=slim.BF16, lim=None, W=16, wdt=slim.BF16, out=4, n=64, H=20, dh=64, T=1500,
+              scale=0.125, opt=0, ws=256, wsb=1 << 30, stream=None)
+
+    def call(**o):
+        a = dict(ok)
+        a.update(o)
+        return f(a["Q"], a["K"], a["kdt"], a["lim"], a["W"], a["wdt"], a["out"], a["n"], a["H"], a["dh"],
+                 a["T"], a["scale"], a["opt"], a["ws"], a["wsb"], a["stream"])
+    for field in ("Q", "K", "W", "out", "ws"):
+        assert call(**{field: None}) == 1, field
+    assert call(opt=3) == 1 and call(opt=-1) == 1
+    assert call(n=0) == 1 and call(T=0) == 1
+    assert call(Q=20) == 1                      # Q rows are read 16 bytes at a time
+    assert call(lim=6) == 1                     # limits not 4-byte aligned
+    assert call(kdt=slim.F32) == 2              # bf16 context only
+    assert call(dh=32, H=40) == 2               # dh 64 or 128
+    assert call(dh=64, H=3) == 2                # d a multiple of 128
+    assert call(wdt=7) == 2
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 128, 131072), (64, 20, 64, 1500), (2048, 12, 64, 2048),
+                                   (63, 20, 64, 1500), (66, 20, 64, 1500), (5, 2, 64, 7), (300, 32, 128, 512)])
+def test_multi_query_option_follows_the_cost_model(slim, shape):
+    """The library's option choice is the cheaper option by the multiply-
+    accumulate counts the oracle states (ties go to option 2)."""
+    n, H, dh, T = shape
+    c = oracle.multi_query_cost(n, H, T, H * dh)
+    want = 1 if c["opt1"] < c["opt2"] else 2
+    assert slim.multi_query_option(n, H, dh, T) == want
