@@ -166,6 +166,108 @@ __global__ void __launch_bounds__(512) qk_proj_kernel(const float* __restrict__ 
   }
 }
 
+// Many sequences (B >= 8): the same product on MFMA.  x is fp32; it is
+// split into three bf16 parts x = hi + mid + lo (together they carry fp32's
+// 24 significant bits), each multiplied by bf16 W on 32x32x8 MFMA with fp32
+// accumulation, so every product is exact and only the accumulation rounds,
+// as on the vector path.  Workgroup: 32 sequences x 256 columns of [q | k]
+// (four waves of 64) x KR rows of W in 64-row blocks; the W block sits in LDS
+// row-major (transpose reads give the B operands), the x block as its three
+// bf16 parts (one 8-byte read per A operand).
+constexpr int kQmCols = 256, kQmRows = 64;
+constexpr int kQmWPitch = kQmCols * 2 + 16;  // bytes per W row in LDS
+constexpr int kQmXPitch = kQmRows * 2 + 8;   // bytes per x row (one part) in LDS
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_q;
+
+__global__ void __launch_bounds__(256) qk_mfma_kernel(const float* __restrict__ x, const uint16_t* __restrict__ WQ,
+                                                      const uint16_t* __restrict__ WK, float* __restrict__ part,
+                                                      int B, int d, int KR) {
+  __shared__ __attribute__((aligned(16))) char Ws[kQmRows * kQmWPitch];
+  __shared__ __attribute__((aligned(16))) char Xs[3 * 32 * kQmXPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int n2 = 2 * d;
+  const int c0 = blockIdx.x * kQmCols;
+  const int k0 = blockIdx.y * KR, k1 = min(d, k0 + KR);
+  const int b0 = blockIdx.z * 32;
+
+  // staging: 8 chunks of W (row c/32, 8 columns at 8*(c%32)) and 8 x values
+  uint4 sw[8];
+  float sx[8];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 5, col = c0 + (c & 31) * 8;
+      sw[i] = make_uint4(0, 0, 0, 0);
+      if (kb + r < k1 && col < n2) {
+        const uint16_t* Wm = col < d ? WQ : WK;
+        sw[i] = *reinterpret_cast<const uint4*>(Wm + (size_t)(kb + r) * d + (col < d ? col : col - d));
+      }
+      const int xb = c >> 6, xk = c & 63;  // 32 sequences x 64 rows
+      sx[i] = (b0 + xb < B && kb + xk < k1) ? x[(size_t)(b0 + xb) * d + kb + xk] : 0.f;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(Ws + (c >> 5) * kQmWPitch + (c & 31) * 16) = sw[i];
+      const int xb = c >> 6, xk = c & 63;
+      const float v = sx[i];
+      const uint32_t hi = f32_to_bf16_rne(v);
+      const float r1 = v - __uint_as_float(hi << 16);
+      const uint32_t mid = f32_to_bf16_rne(r1);
+      const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+      char* px = Xs + xb * kQmXPitch + xk * 2;
+      *reinterpret_cast<uint16_t*>(px) = (uint16_t)hi;
+      *reinterpret_cast<uint16_t*>(px + 32 * kQmXPitch) = (uint16_t)mid;
+      *reinterpret_cast<uint16_t*>(px + 64 * kQmXPitch) = (uint16_t)lo;
+    }
+  };
+
+  f32x16 acc[2] = {f32x16{0}, f32x16{0}};
+  // A operands: sequence lane%32, rows 8*kk + 4*h .. +3 of each part
+  const char* xa = Xs + (lane & 31) * kQmXPitch + h * 8;
+  // B operands by transpose read (as in the prefill GEMM): lane L points at
+  // columns 16*((L/16)%2) + 4*(L%4) of W row 4*(L/32) + (L%16)/4 of a
+  // 32-column tile and an 8-row step
+  const uint32_t wb = (uint32_t)(uintptr_t)Ws + (uint32_t)((4 * h + ((lane & 15) >> 2)) * kQmWPitch +
+                                                           (wave * 64 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+  load(k0);
+  for (int kb = k0; kb < k1; kb += kQmRows) {
+    store();
+    __syncthreads();
+    if (kb + kQmRows < k1) load(kb + kQmRows);
+#pragma unroll
+    for (int kk = 0; kk < kQmRows / 8; ++kk) {
+      s16x4 a[3], bo[2];
+#pragma unroll
+      for (int p3 = 0; p3 < 3; ++p3) a[p3] = *reinterpret_cast<const s16x4*>(xa + p3 * 32 * kQmXPitch + 16 * kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_q*)(size_t)(wb + (uint32_t)(8 * kk * kQmWPitch + 64 * j)));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int p3 = 0; p3 < 3; ++p3)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a[p3], bo[j], acc[j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = c0 + wave * 64 + 32 * j + (lane & 31);
+    if (col >= n2) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int b = b0 + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (b < B) part[((size_t)blockIdx.y * B + b) * n2 + col] = acc[j][e];
+    }
+  }
+}
+
 constexpr int kQkSumBatch = 32;  // partials loaded together per output
 
 template <bool KBF16>
@@ -201,6 +303,27 @@ __global__ void __launch_bounds__(256) qk_finish_kernel(const float* __restrict_
 
 bool make_step_plan(int B, int d, int ncu, bool w_bf16, size_t base, StepPlan* p) {
   if (B <= 0 || d <= 0 || d % 8 != 0) return false;
+  p->mfma = w_bf16 && B >= 8;
+  if (p->mfma) {  // 256-column tiles x 32 sequences; row blocks of 64 rows for about one round
+    const int ntile = (2 * d + kQmCols - 1) / kQmCols, mg = (B + 31) / 32;
+    const int nblk = (d + kQmRows - 1) / kQmRows;
+    long long ks = (long long)ncu / ((long long)ntile * mg);
+    if (ks < 1) ks = 1;
+    if (ks > nblk) ks = nblk;
+    p->kr = (int)((nblk + ks - 1) / ks) * kQmRows;
+    p->ks = (d + p->kr - 1) / p->kr;
+    p->ntile = ntile;
+    p->bgroups = mg;
+    p->bg = 32;
+    p->nb = 0;
+    size_t off = (base + 255) & ~(size_t)255;
+    p->off_q = off;
+    off += ((size_t)B * d * sizeof(float) + 255) & ~(size_t)255;
+    p->off_part = off;
+    off += ((size_t)p->ks * B * 2 * d * sizeof(float) + 255) & ~(size_t)255;
+    p->bytes = off;
+    return true;
+  }
   p->bg = B >= 16 ? 16 : (B > 8 ? 16 : (B > 4 ? 8 : (B > 2 ? 4 : B)));
   const int ntile = (2 * d + kQkCols - 1) / kQkCols;
   const int bgroups = (B + p->bg - 1) / p->bg;
@@ -270,8 +393,15 @@ hipError_t launch_step_qk(const StepPlan& p, const float* x, const void* WQ, con
                           int d, int T_max, char* ws, hipStream_t s) {
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   float* q = reinterpret_cast<float*>(ws + p.off_q);
-  hipError_t e = w_bf16 ? launch_proj_bg<true>(p, x, WQ, WK, part, B, d, s)
-                        : launch_proj_bg<false>(p, x, WQ, WK, part, B, d, s);
+  hipError_t e;
+  if (p.mfma) {
+    hipLaunchKernelGGL(qk_mfma_kernel, dim3(p.ntile, p.ks, p.bgroups), dim3(256), 0, s, x,
+                       static_cast<const uint16_t*>(WQ), static_cast<const uint16_t*>(WK), part, B, d, p.kr);
+    e = hipGetLastError();
+  } else {
+    e = w_bf16 ? launch_proj_bg<true>(p, x, WQ, WK, part, B, d, s)
+               : launch_proj_bg<false>(p, x, WQ, WK, part, B, d, s);
+  }
   if (e != hipSuccess) return e;
   const long long n = (long long)B * 2 * d;
   const unsigned grid = (unsigned)((n + 255) / 256);

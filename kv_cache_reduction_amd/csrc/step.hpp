@@ -10,6 +10,7 @@ namespace slim {
 // [q | k] = x . [W_Q | W_K] as ks row blocks of kr rows of W, each workgroup
 // 512 output columns of BG = bg sequences; partial sums [ks][B][2d] float.
 struct StepPlan {
+  bool mfma;  // bf16 W and B >= 8: the MFMA product (qk_mfma_kernel), else the vector one
   int bg, bgroups, ntile, ks, kr, nb;  // nb: row batches per wave (kr = 8 waves x batch rows x nb)
   size_t off_q;     // [B, d] float: the new queries
   size_t off_part;  // [ks, B, 2d] float
