@@ -44,6 +44,8 @@
 //    l of every head.  q is pre-scaled by scale*log2(e); exponentials use
 //    v_exp_f32.
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -390,10 +392,14 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
 // no score is computed twice.
 //
 // Scores of step j are formed kXchgLook steps ahead (in step j-3) and
-// published as 64-bit mailbox entries {tag, score}; tag = launch epoch and
-// step index, so a reader can tell a fresh entry from an old one without
-// any ordering between entries (relaxed agent-scope atomics: no fences, no
-// drain of the DMA queue).  In step i a wave
+// published as 64-bit mailbox entries {tag, score}; the 32-bit tag holds 24
+// bits of a per-launch epoch (seeded at random per process, so stale
+// entries left in reused memory by another launch or process do not match)
+// and 8 bits of the entry's use count in its ring slot (step / 8: a slot
+// holds step j only after step j-8, and the two workgroups of a pair stay
+// within a few steps of each other).  A reader thus tells a fresh entry from
+// an old one without any ordering between entries (relaxed agent-scope
+// atomics: no fences, no drain of the DMA queue).  In step i a wave
 //   1. checks the partner's entries of step i+1 (loaded by LDS DMA during
 //      step i-1) and copies them into the score buffer,
 //   2. starts the load of the partner's entries of step i+2,
@@ -416,7 +422,7 @@ struct XchgParams {
   AttendBf16Params a;
   unsigned long long* mbox;     // [nch][2][kMboxDepth][8 waves][16] {tag, score}
   unsigned long long* tickets;  // arrival counter (any initial value)
-  uint32_t epoch;            // 16 bits used
+  uint32_t epoch;            // 24 bits used
 };
 
 __device__ __forceinline__ void dma16_sc1(uint32_t lds, const i32x4& rsrc, uint32_t voff) {
@@ -489,7 +495,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   const uint32_t poll_lds = (uint32_t)reinterpret_cast<uintptr_t>(pollbuf + wave * 32);
   const int r16 = lane & 15;
   const int pub_e = (l32 >> 4) * 8 + half * 4 + 2 * (r16 & 1) + (r16 >> 1);  // valid for r16 < 4
-  const uint32_t ep = (xp.epoch & 0xffffu) << 16;
+  const uint32_t ep = (xp.epoch & 0xffffffu) << 8;
   bool failed = false;
 
   int gstep = 0;  // step counter across pieces (tags, score buffers)
@@ -528,7 +534,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
       if (r16 < 4) {
         S[(gs & (NS - 1)) * 256 + (ocol / DH) * 8 + (pub_e & 7)] = x;
         const unsigned long long ent =
-            ((unsigned long long)(ep | ((uint32_t)gs & 0xffffu)) << 32) | __float_as_uint(x);
+            ((unsigned long long)(ep | (((uint32_t)gs / kMboxDepth) & 0xffu)) << 32) | __float_as_uint(x);
         __hip_atomic_store(mine + (size_t)((uint32_t)gs % kMboxDepth) * 8 * 16 + pub_e, ent, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -544,7 +550,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
     // carry the step's tag; returns false (S untouched) otherwise
     auto try_check = [&](int step) -> bool {
       const int gs = gstep + step;
-      const uint32_t want = ep | ((uint32_t)gs & 0xffffu);
+      const uint32_t want = ep | (((uint32_t)gs / kMboxDepth) & 0xffu);
       const unsigned long long v = lane < 16 ? pollbuf[wave * 32 + (gs & 1) * 16 + lane] : 0ull;
       const bool ok = __all(lane >= 16 || (uint32_t)(v >> 32) == want);
       if (ok && lane < 16)
@@ -710,10 +716,15 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   return hipGetLastError();
 }
 
-// Per-launch epoch of the mailbox tags: distinct for consecutive launches of
-// the process.
+// Per-launch epoch of the mailbox tags (24 bits used): distinct for 2^24
+// consecutive launches of the process, and started at a random value so
+// that another process's entries left in reused device memory do not match.
+static uint32_t epoch_seed() {
+  std::random_device rd;
+  return rd() ^ (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count();
+}
 static uint32_t next_epoch() {
-  static std::atomic<uint32_t> ctr{0x5a17u};
+  static std::atomic<uint32_t> ctr{epoch_seed()};
   return ctr.fetch_add(1) + 1;
 }
 
