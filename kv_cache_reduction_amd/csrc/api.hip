@@ -1,6 +1,7 @@
 // C ABI of libslim.so: argument checks, launch planning and dispatch.
 // Every entry point validates its arguments on the host before enqueueing
 // anything and maps failures to slim_status_t; no exception crosses the ABI.
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -11,6 +12,7 @@
 #include "internal.hpp"
 #include "step.hpp"
 #include "multi.hpp"
+#include "launch.hpp"
 
 namespace slim {
 
@@ -24,17 +26,21 @@ int env_int(const char* name, int dflt) {
 }
 
 static int device_cus(int* ncu) {
-  static int cache[64];  // 0 = unknown
+  static std::atomic<int> cache[kMaxDevices];  // 0 = unknown
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *ncu = cache[dev];
-    return 0;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *ncu = c;
+      return 0;
+    }
   }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return -1;
-  if (dev >= 0 && dev < 64) cache[dev] = n;
+  if (cached) cache[dev].store(n, std::memory_order_relaxed);
   *ncu = n;
   return 0;
 }

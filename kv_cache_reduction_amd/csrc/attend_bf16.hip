@@ -49,6 +49,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "launch.hpp"
 
 namespace slim {
 
@@ -705,13 +706,9 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   p.qscale = a.scale * kLog2e;
   const size_t lds = (size_t)pl.nw * WB + (512 + 16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_bf16_kernel<DH, GC, NST>;
-  static int lds_allowed = 0;  // largest dynamic LDS size already granted to this kernel
-  if ((int)lds > lds_allowed) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    lds_allowed = (int)lds;
-  }
+  static std::atomic<int> granted[kMaxDevices];
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), lds, granted);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.nch * GC), dim3(pl.nw * 64), lds, s, p);
   return hipGetLastError();
 }
@@ -755,14 +752,10 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   const size_t lds = (size_t)pl.nw * NST * 4 * (1024 + 64) + 4 * 256 * sizeof(float) +
                      (size_t)pl.nw * 32 * sizeof(unsigned long long) + (16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_xchg_kernel<NST>;
-  static int lds_allowed = 0;
-  if ((int)lds > lds_allowed) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess) {
-      (void)hipGetLastError();
-      return hipErrorNotSupported;
-    }
-    lds_allowed = (int)lds;
+  static std::atomic<int> granted[kMaxDevices];
+  if (allow_lds(reinterpret_cast<const void*>(kern), lds, granted) != hipSuccess) {
+    (void)hipGetLastError();
+    return hipErrorNotSupported;
   }
   hipLaunchKernelGGL(kern, dim3(pl.nch * 2), dim3(pl.nw * 64), lds, s, xp);
   return hipGetLastError();

@@ -35,6 +35,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "multi.hpp"
+#include "launch.hpp"
 
 namespace slim {
 
@@ -332,11 +333,9 @@ static hipError_t launch_mq(const MultiPlan& pl, const MultiParams& mp, hipStrea
   using S = MultiShape<DH, OPT>;
   const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * 4 + 16;
   auto kern = multi_attend_kernel<DH, QW, OPT>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  static std::atomic<int> granted[kMaxDevices];
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), lds, granted);
+  if (e != hipSuccess) return e;
   const int nqg = (mp.n + 32 * QW - 1) / (32 * QW);
   const int ncb = OPT == 2 ? (mp.d + S::NCW - 1) / S::NCW : 1;
   hipLaunchKernelGGL(kern, dim3(ncb, mp.H * nqg, pl.nsplit), dim3(64 * QW), lds, s, mp);
