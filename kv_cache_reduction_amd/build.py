@@ -23,10 +23,10 @@ LIB = os.path.join(HERE, "libslim.so")
 HIP_SOURCES = ["api.hip", "attend_bf16.hip", "attend_f32.hip", "finish.hip", "mha_kv.hip",
                "multi.hip", "prefill.hip", "probe.hip", "step.hip"]
 CPP_SOURCES = ["wkv_host.cpp"]
-# The bf16 attend kernel never sees NaN in the rows it reads (it only takes
-# maxima of finite scores and -inf); without this flag every fmaxf first
-# quiets possible signalling NaNs with an extra instruction.
-EXTRA_FLAGS = {"attend_bf16.hip": ["-fno-honor-nans"]}
+# The bf16 attend and many-query kernels never see NaN in the rows they read
+# (they only take maxima of finite scores and -inf); without this flag every
+# fmaxf first quiets possible signalling NaNs with an extra instruction.
+EXTRA_FLAGS = {"attend_bf16.hip": ["-fno-honor-nans"], "multi.hip": ["-fno-honor-nans"]}
 ARCH = os.environ.get("SLIM_OFFLOAD_ARCH", "gfx950")
 
 

@@ -43,6 +43,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_m;
 
 constexpr int kMTile = 32;              // context rows per tile
 constexpr float kMultiSlack = 8.f;      // log2 units
+constexpr uint32_t kOnes2 = 0x3f803f80u;  // two bf16 1.0
 
 struct MultiParams {
   const float* Q;          // [n, d]
@@ -200,19 +201,22 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
         sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, ql[k], sc, 0, 0, 0);
       }
     }
-    float v[4][4];
+    // rows past a query's limit (or the split) are -inf; only tiles that
+    // cross a limit of this wave need the per-element test
+    float v[16];
+    if (__builtin_amdgcn_ballot_w64(tb + kMTile > min(lim, t_end)) == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+      for (int i = 0; i < 16; ++i) v[i] = sc[i];
+    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 8 * k + 4 * hh + j;
-        v[k][j] = (tb + t < min(lim, t_end)) ? sc[4 * k + j] : kNegInf;
+      for (int i = 0; i < 16; ++i) {
+        const int t = 8 * (i >> 2) + 4 * hh + (i & 3);
+        v[i] = (tb + t < min(lim, t_end)) ? sc[i] : kNegInf;
       }
+    }
     float mx = kNegInf;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, v[k][j]);
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, v[i]);
     mx = pair_max(mx);
     const bool up = mx > m_ref + kMultiSlack;
     if (__builtin_amdgcn_ballot_w64(up)) {  // some row moves its reference: rescale through LDS
@@ -228,17 +232,18 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
         for (int s = 0; s < S::NCT; ++s) acc[s][i] *= a;
       }
     }
+    // weights 2^(s - m) rounded to bf16 (hardware pack), and the normaliser
+    // summed from the same rounded weights the MFMA uses; m is finite once
+    // any score of the row was, masked scores give 0 either way
+    const float mu = fmaxf(m_ref, -__FLT_MAX__);
     s16x4 pa[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        e[j] = v[k][j] == kNegInf ? 0.f : fast_exp2(v[k][j] - m_ref);
-        l_half += e[j];
-      }
-      pa[k] = s16x4{(short)f32_to_bf16_rne(e[0]), (short)f32_to_bf16_rne(e[1]),
-                    (short)f32_to_bf16_rne(e[2]), (short)f32_to_bf16_rne(e[3])};
+      const bf16x2_t p01 = {(__bf16)fast_exp2(v[4 * k] - mu), (__bf16)fast_exp2(v[4 * k + 1] - mu)};
+      const bf16x2_t p23 = {(__bf16)fast_exp2(v[4 * k + 2] - mu), (__bf16)fast_exp2(v[4 * k + 3] - mu)};
+      const uint32_t w0 = __builtin_bit_cast(uint32_t, p01), w1 = __builtin_bit_cast(uint32_t, p23);
+      l_half = dot2_bf16(w1, kOnes2, dot2_bf16(w0, kOnes2, l_half));
+      pa[k] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
     }
     // P . value block
 #pragma unroll
