@@ -72,7 +72,7 @@ template <int DH, int OPT>
 struct MultiShape {
   static constexpr int NCW = OPT == 2 ? 128 : DH;     // value columns per workgroup
   static constexpr int NCT = NCW / 32;                // 32-column MFMA tiles per wave
-  static constexpr int SP = DH * 2 + 8;               // bytes per score row in LDS
+  static constexpr int SP = DH * 2 + 16;              // bytes per score row in LDS
   static constexpr int VP = NCW * 2 + 16;             // bytes per value row in LDS
   static constexpr int SCH = kMTile * DH / 8;         // 16-byte chunks of the score part
   static constexpr int VCH = kMTile * NCW / 8;        // 16-byte chunks of the value part
@@ -130,40 +130,42 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     }
   }
 
-  // tile loads: chunk c < SCH is score row c / (DH/8), 8 columns at 8*(c % (DH/8));
-  // the rest are value rows.  Rows past T are clamped (masked later).
+  // tile loads: chunk c < SCH is score row c / (DH/8), 8 columns at
+  // 8*(c % (DH/8)); the rest are value rows.  Each thread's chunks are fixed,
+  // so their sources (row 0 of the tile), rows and LDS offsets are computed
+  // once; rows past T are clamped (and masked later).
+  const uint16_t* ch_src[CPT];
+  int ch_row[CPT];
+  uint32_t ch_lds[CPT];
+  bool ch_ok[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + NT * i;
+    ch_ok[i] = c < S::SCH + S::VCH;
+    if (c < S::SCH) {
+      const int r = c / (DH / 8), k8 = c - r * (DH / 8);
+      ch_row[i] = r;
+      ch_src[i] = p.K + h * DH + 8 * k8;
+      ch_lds[i] = (uint32_t)(r * S::SP + 16 * k8);
+    } else {
+      const int cc = ch_ok[i] ? c - S::SCH : 0, r = cc / (S::NCW / 8), k8 = cc - r * (S::NCW / 8);
+      ch_row[i] = r;
+      ch_src[i] = p.Vs + min(c0 + 8 * k8, d - 8);
+      ch_lds[i] = (uint32_t)(kMTile * S::SP + r * S::VP + 16 * k8);
+    }
+  }
   uint4 stage[CPT];
   auto load_tile = [&](int tb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < S::SCH) {
-        const int r = c / (DH / 8), k8 = c - r * (DH / 8);
-        const int row = min(tb + r, p.T - 1);
-        v = *reinterpret_cast<const uint4*>(p.K + (size_t)row * d + h * DH + 8 * k8);
-      } else if (c < S::SCH + S::VCH) {
-        const int cc = c - S::SCH, r = cc / (S::NCW / 8), k8 = cc - r * (S::NCW / 8);
-        const int row = min(tb + r, p.T - 1);
-        const int col = min(c0 + 8 * k8, d - 8);
-        v = *reinterpret_cast<const uint4*>(p.Vs + (size_t)row * d + col);
-      }
-      stage[i] = v;
+      const int row = min(tb + ch_row[i], p.T - 1);
+      stage[i] = ch_ok[i] ? *reinterpret_cast<const uint4*>(ch_src[i] + (size_t)row * d) : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_tile = [&](char* buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
-      if (c < S::SCH) {
-        const int r = c / (DH / 8), k8 = c - r * (DH / 8);
-        *reinterpret_cast<uint2*>(buf + r * S::SP + 16 * k8) = make_uint2(stage[i].x, stage[i].y);
-        *reinterpret_cast<uint2*>(buf + r * S::SP + 16 * k8 + 8) = make_uint2(stage[i].z, stage[i].w);
-      } else if (c < S::SCH + S::VCH) {
-        const int cc = c - S::SCH, r = cc / (S::NCW / 8), k8 = cc - r * (S::NCW / 8);
-        *reinterpret_cast<uint4*>(buf + kMTile * S::SP + r * S::VP + 16 * k8) = stage[i];
-      }
-    }
+    for (int i = 0; i < CPT; ++i)
+      if (ch_ok[i]) *reinterpret_cast<uint4*>(buf + ch_lds[i]) = stage[i];
   };
 
   float* rv = rowv + wave * 32;
