@@ -393,8 +393,8 @@ def cpu_baseline(name, T_sample=16384, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
-              f"of this path is described in DESIGN.md and not run", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path's sharding over "
+              f"several GPUs is a design, not built or run here", file=sys.stderr)
         sys.exit(2)
     import torch
     import kv_cache_reduction_amd as slim

@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) on hosts without a visible GPU so the
-    # CPU suite stays green here; on the GPU machine they run.
+    # GPU tests are skipped (not failed) on hosts without a visible GPU, so the
+    # CPU suite stays green there; where an MI355X is visible they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
