@@ -454,7 +454,8 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   char* ring = reinterpret_cast<char*>(smem);                                 // [nw][NST][SB]
   float* S = reinterpret_cast<float*>(ring + (size_t)nw * NST * SB);           // [NS][32][8]
   unsigned long long* pollbuf = reinterpret_cast<unsigned long long*>(S + NS * 256);  // [nw][2][16]
-  int* tmp = reinterpret_cast<int*>(pollbuf + nw * 32);                         // [16]
+  float* qbuf = reinterpret_cast<float*>(pollbuf + nw * 32);                    // [nw][256] q of each unit
+  int* tmp = reinterpret_cast<int*>(qbuf + nw * kMfmaUnitCols);                 // [16]
   int* pre = tmp + 16;                                                          // [B+1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -464,8 +465,9 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   // once, whatever the counter held before, and a workgroup's partner is
   // the next or previous arrival (one pair wraps from the first arrival to
   // the last), so a resident workgroup never waits on one that cannot be
-  // scheduled.
-  if (tid == 0)
+  // scheduled.  (Taken in wave 1, so that its round trip overlaps wave 0's
+  // read of the lengths.)
+  if (tid == 64)
     tmp[15] = (int)(__hip_atomic_fetch_add(xp.tickets, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) %
                     (unsigned long long)gridDim.x);
   for (int i = tid; i < NS * 256; i += blockDim.x) S[i] = kNegInf;
@@ -494,6 +496,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   unsigned long long* mine = xp.mbox + ((size_t)(2 * c + cg) * kMboxDepth * 8 + wave) * 16;
   const unsigned long long* theirs = xp.mbox + ((size_t)(2 * c + 1 - cg) * kMboxDepth * 8 + wave) * 16;
   const uint32_t poll_lds = (uint32_t)reinterpret_cast<uintptr_t>(pollbuf + wave * 32);
+  const uint32_t qbuf_s = (uint32_t)reinterpret_cast<uintptr_t>(qbuf + wave * kMfmaUnitCols);
   const int r16 = lane & 15;
   const int pub_e = (l32 >> 4) * 8 + half * 4 + 2 * (r16 & 1) + (r16 >> 1);  // valid for r16 < 4
   const uint32_t ep = (xp.epoch & 0xffffffu) << 8;
@@ -508,8 +511,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
     const int n = min(cend, s1) - s0 - tb;
     const int slot = c + b;
 
-    uint4 qh, ql;
-    split_q8(p.q + (size_t)b * d + ocol, p.qscale, qh, ql);
+    uint4 qh, ql;  // split in the prologue, from the wave's q columns brought to LDS
 
     const uint16_t* kbase = p.K + ((size_t)b * p.T_max + tb) * d;
     const uint32_t nbytes = (uint32_t)n * row_bytes;
@@ -594,13 +596,20 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 
     // prologue: ring steps 0..3 landed; the own heads' scores of steps 0..2
     // published and the partner's of step 0 in S; B operands of step 0;
-    // step 4 in flight.
+    // step 4 in flight.  The wave's 1 KB of q travels by DMA with the first
+    // ring steps, and each step's scores go out as soon as that step has
+    // landed (the waits count only the younger ring loads).
     s16x4 bcur[8];
+    dma16(qbuf_s, buffer_desc(p.q + (size_t)b * d + ubase, kMfmaUnitCols * 4u), 16u * lane);
 #pragma unroll
     for (int s = 0; s < NST; ++s) issue(s);
-    wait_vmcnt<0>();
+    wait_vmcnt<NST * LPS>();
+    split_q8(qbuf + wave * kMfmaUnitCols + 8 * l32, p.qscale, qh, ql);
+    wait_vmcnt<3 * LPS>();
     publish(0);
+    wait_vmcnt<2 * LPS>();
     publish(1);
+    wait_vmcnt<LPS>();
     publish(2);
     wait_lgkmcnt0();
     poll(0);
@@ -726,11 +735,13 @@ static uint32_t next_epoch() {
 }
 
 // Launches the exchange kernel when the shape allows it (two full column
-// groups of dh = 128); returns hipErrorNotSupported otherwise, and the caller
-// falls back.
+// groups of dh = 128) and q is 16-byte aligned (it is brought to LDS by
+// 16-byte DMA); returns hipErrorNotSupported otherwise, and the caller falls
+// back.
 static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = 4;
-  if (!pl.xchg || env_int("SLIM_XCHG", 1) == 0) return hipErrorNotSupported;
+  if (!pl.xchg || (reinterpret_cast<uintptr_t>(a.q) & 15u) != 0 || env_int("SLIM_XCHG", 1) == 0)
+    return hipErrorNotSupported;
   XchgParams xp;
   AttendBf16Params& p = xp.a;
   p.q = a.q;
@@ -750,7 +761,8 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   xp.tickets = reinterpret_cast<unsigned long long*>(a.ws + pl.off_tickets);
   xp.epoch = next_epoch();
   const size_t lds = (size_t)pl.nw * NST * 4 * (1024 + 64) + 4 * 256 * sizeof(float) +
-                     (size_t)pl.nw * 32 * sizeof(unsigned long long) + (16 + (size_t)a.B + 1) * sizeof(int);
+                     (size_t)pl.nw * 32 * sizeof(unsigned long long) + (size_t)pl.nw * kMfmaUnitCols * sizeof(float) +
+                     (16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_xchg_kernel<NST>;
   static std::atomic<int> granted[kMaxDevices];
   if (allow_lds(reinterpret_cast<const void*>(kern), lds, granted) != hipSuccess) {

@@ -271,3 +271,28 @@ def test_score_exchange_and_fallback(monkeypatch, xchg):
     ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
     assert np.all(o[3] == 0)
     _check(f"xchg={xchg}", o, ref, TOL["bf16"])
+
+
+def test_exchange_shape_with_q_4_byte_aligned():
+    """q only 4-byte aligned (a view one float into a buffer).  The exchange
+    kernel reads q by 16-byte DMA, so the launcher takes the general
+    two-column-group kernel for it; the result still matches the oracle and
+    equals, to the bf16 tolerance, the call with an aligned q."""
+    import torch
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS["c2"], B=3, T_max=700, len_lo=1, len_hi=700)
+    wl = syn.make(cfg)
+    K = syn.k_cache(cfg, wl.w, np.minimum(wl.lengths, cfg.T_max))
+    Kd, Wd = to_dev(K), dev_wkv(cfg, wl.w.W_K, wl.w.W_V)
+    flat = torch.zeros(cfg.B * cfg.d + 4, dtype=torch.float32, device="cuda")
+    qv = flat[1:1 + cfg.B * cfg.d].view(cfg.B, cfg.d)
+    qv.copy_(to_dev(wl.q.astype(np.float32)))
+    assert qv.data_ptr() % 16 == 4
+    out = torch.empty((cfg.B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
+    slim.decode(qv, Kd, to_dev(wl.lengths.astype(np.int32)), Wd, out, cfg.H, cfg.dh, cfg.scale)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    ref = oracle_decode(cfg, wl.q, K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("q at a 4-byte offset", o, ref, TOL["bf16"])
+    o16 = gpu_decode(cfg, wl.q, Kd, wl.lengths, Wd)
+    assert oracle.err_rel(o, o16) <= TOL["bf16"]
