@@ -82,7 +82,8 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   p->nslots = p->nch + B - 1;
   {
     const int big = proj_rows(dh, true);
-    const long long grid = (long long)H * ((d + big - 1) / big) * ((B + 7) / 8);
+    p->spw = finish_seqs(H, (d + big - 1) / big, B, ncu);
+    const long long grid = (long long)H * ((d + big - 1) / big) * ((B + p->spw - 1) / p->spw);
     p->proj_rows = grid * 2 >= ncu ? big : proj_rows(dh, false);
   }
   p->npc = (d + p->proj_rows - 1) / p->proj_rows;

@@ -6,8 +6,10 @@
 // Partials (written by the attend phase) are laid out U[h][slot][d] and
 // ml[slot][2][H] (running max in log2 units, normaliser).
 //
-// merge_project  grid (H, ceil(d/R), ceil(B/8)), R rows of W_KV per
-//          workgroup (256, or 64 when that grid would be small).  For each of its (up to 8) sequences b the
+// merge_project  grid (H, ceil(d/R), ceil(B/S)), R rows of W_KV per
+//          workgroup (256, or 64 when that grid would be small) and S = 8
+//          or 16 sequences (16 while that grid still fills the device, so
+//          that W_KV is read half as often).  For each of its sequences b the
 //          workgroup first merges the slots s of b over its R rows
 //          (log-sum-exp):
 //            m* = max_s m_s,  l* = sum_s 2^(m_s - m*) l_s,
@@ -16,7 +18,7 @@
 //          threads' sums combined the same way),
 //          then multiplies by the W_KV rows it holds in registers:
 //            part[rb, b, h, j] = sum_{r in rows} u[r] W_KV[r, h*dh + j].
-//          The partials are read once and W_KV once per 8 sequences.
+//          The partials are read once and W_KV once per S sequences.
 // reduce   out[b, h, j] = sum_rb part[rb, b, h, j] in a fixed order, so the
 //          result does not depend on scheduling.
 #include "common.hpp"
@@ -25,7 +27,6 @@
 
 namespace slim {
 
-constexpr int kSeqPerProj = 8;  // sequences per workgroup
 constexpr int kMergeBatch = 4;  // slots whose loads a thread issues together
 
 template <int DH, bool WBF16, int PR>
@@ -34,7 +35,8 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
                                                             const float* __restrict__ ml,
                                                             const void* __restrict__ W,
                                                             float* __restrict__ part, int B, int H, int d,
-                                                            int T_max, int nch, int nslots, int fixed_ns) {
+                                                            int T_max, int nch, int nslots, int fixed_ns,
+                                                            int spw) {
   // projection: thread t covers JW output columns (group jq = t % JQ) over the
   // rows of subset t / JQ
   constexpr int JQ = DH >= 8 ? DH / 8 : 1;  // column groups per head
@@ -51,13 +53,13 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   int* tmp = smem;                                       // [8]
   float* red = reinterpret_cast<float*>(smem + 8);       // [max(NSS * PR, NRS * DH)]
   constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
-  float* us = red + RED;                                 // [8][PR]
-  float* mstar = us + kSeqPerProj * PR;                  // [NSS][2]: running max, normaliser
+  float* us = red + RED;                                 // [spw][PR]
+  float* mstar = us + spw * PR;                          // [NSS][2]: running max, normaliser
   int* pre = reinterpret_cast<int*>(mstar + 2 * NSS);    // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * kSeqPerProj;
-  const int nr = min(PR, d - r0), nb = min(kSeqPerProj, B - b0);
+  const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * spw;
+  const int nr = min(PR, d - r0), nb = min(spw, B - b0);
 
   // W_KV rows [r0, r0 + PR) of head h's columns, in registers.  The loads
   // are unconditional (rows past the block clamped, then zeroed) so that
@@ -246,10 +248,11 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   const float* U = reinterpret_cast<const float*>(a.ws + pl.off_U);
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
-  const size_t lds = (8 + (size_t)RED + kSeqPerProj * PR + 2 * NSS + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
+  const int spw = pl.spw == 16 ? 16 : 8;
+  const size_t lds = (8 + (size_t)RED + (size_t)spw * PR + 2 * NSS + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
   hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR>),
-                     dim3(a.H, pl.npc, (a.B + kSeqPerProj - 1) / kSeqPerProj), dim3(256), lds, s, a.lengths,
-                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns);
+                     dim3(a.H, pl.npc, (a.B + spw - 1) / spw), dim3(256), lds, s, a.lengths,
+                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;

@@ -19,6 +19,7 @@ struct DecodePlan {
   int nch;         // token chunks
   int nslots;      // partial slots
   int proj_rows;   // W_KV rows per finish workgroup (proj_rows(dh, large or not))
+  int spw;         // sequences per finish workgroup (finish_seqs)
   int npc;         // W_KV row blocks of the finish (proj_rows rows each)
   size_t off_U;    // [H, nslots, d] float: unnormalised softmax.K rows per chunk
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
@@ -48,6 +49,11 @@ struct DecodeArgs {
 // times the workgroups.  dh = 256 keeps 64 rows to stay out of spills.
 constexpr int proj_rows(int dh, bool large) {
   return dh > 128 ? 64 : (large ? 256 : (256 / (dh >= 8 ? dh / 8 : 1) > 64 ? 256 / (dh >= 8 ? dh / 8 : 1) : 64));
+}
+// Sequences per finish workgroup: 16 (W_KV read once per 16 sequences) while
+// that grid still gives every compute unit two workgroups, else 8.
+inline int finish_seqs(int H, int npc_big, long long B, int ncu) {
+  return B > 8 && (long long)H * npc_big * ((B + 15) / 16) >= 2LL * ncu ? 16 : 8;
 }
 constexpr int kMfmaUnitCols = 256; // K columns per MFMA unit (32 lanes x 8 columns)
 constexpr int kStepTokens = 8;     // tokens per MFMA step (32x32x8)

@@ -389,7 +389,8 @@ bool make_multi_plan(int n, int H, int dh, int T, int method, bool w_bf16, int n
   if (method == 2) {
     p->fin.nslots = n * p->nsplit;
     const int big = proj_rows(dh, true);
-    const long long grid = (long long)H * ((d + big - 1) / big) * ((n + 7) / 8);
+    p->fin.spw = finish_seqs(H, (d + big - 1) / big, n, ncu);
+    const long long grid = (long long)H * ((d + big - 1) / big) * ((n + p->fin.spw - 1) / p->fin.spw);
     p->fin.proj_rows = grid * 2 >= ncu ? big : proj_rows(dh, false);
     p->fin.npc = (int)((d + p->fin.proj_rows - 1) / p->fin.proj_rows);
     p->fin.nch = 1;
