@@ -120,9 +120,7 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
  * the softmax weights are rounded to bf16 for the MFMA contraction with K.
  * Supported: k_dt bf16 (MFMA path: H <= 32, dh in {32, 64, 128}, d % 8 == 0)
  * or f32 (H <= 64, any dh); w_dt f32 or bf16; B <= 4096.
- * Alignment: K_cache, W_KV and workspace 16 bytes; q, lengths, out 4 bytes
- * (the score-exchange attend kernel of the d = 4096, dh = 128 shapes reads q
- * by 16-byte DMA, so it is used only when q is 16-byte aligned).
+ * Alignment: K_cache, W_KV and workspace 16 bytes; q, lengths, out 4 bytes.
  * Errors: SLIM_ERR_INVALID (null pointers, B/H/dh/T_max <= 0, scale not
  * finite, misaligned pointers), SLIM_ERR_UNSUPPORTED, SLIM_ERR_WORKSPACE,
  * SLIM_ERR_HIP.

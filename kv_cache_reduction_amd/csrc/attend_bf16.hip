@@ -143,7 +143,20 @@ __device__ __forceinline__ void dma16(uint32_t lds, const i32x4& rsrc, uint32_t 
       "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
       :
       : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
+      : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (lane i's dword at lds + 4*i): needs only
+// 4-byte alignment of the source.
+__device__ __forceinline__ void dma4(uint32_t lds, const i32x4& rsrc, uint32_t voff) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
 }
 
 template <int N>
@@ -171,7 +184,8 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
   const int nw = blockDim.x >> 6;
   char* ring = reinterpret_cast<char*>(smem);                     // [nw][NST][SB]
   float* S = reinterpret_cast<float*>(ring + (size_t)nw * WB);     // [2][32][8]
-  int* tmp = reinterpret_cast<int*>(S + 512);                      // [16]
+  float* qbuf = S + 512;                                           // [nw][GC][256] q of the units
+  int* tmp = reinterpret_cast<int*>(qbuf + nw * GC * kMfmaUnitCols);  // [16]
   int* pre = tmp + 16;                                             // [B+1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -239,12 +253,7 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
     const int n = min(cend, s1) - s0 - tb;
     const int slot = c + b;
 
-    uint4 qoh, qol, qxh, qxl;  // scaled query, bf16 hi/lo pairs, own and other unit
-    {
-      const float* qb = p.q + (size_t)b * d;
-      split_q8(qb + (ook ? ocol : 0), p.qscale, qoh, qol);
-      split_q8(qb + (xok ? xcol : 0), p.qscale, qxh, qxl);
-    }
+    uint4 qoh, qol, qxh, qxl;  // scaled query, bf16 hi/lo pairs, own and other unit (prologue)
 
     const uint16_t* kbase = p.K + ((size_t)b * p.T_max + tb) * d;
     const uint32_t nbytes = (uint32_t)n * row_bytes;  // < 2^31 (launch plan)
@@ -289,11 +298,31 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
     for (int s = 0; s < 8; ++s) acc[s] = f32x16{0};
 
     const int nsteps = (n + kStepTokens - 1) / kStepTokens;
-    // prologue: steps 0..NST-1 in flight; scores and B operands of step 0;
-    // step NST refills slot 0
+    // prologue: the wave's q columns (own unit, then the other) travel to
+    // LDS by DMA with steps 0..NST-1; scores and B operands of step 0; step
+    // NST refills slot 0.  (q by plain loads here would make the compiler
+    // wait for the whole burst: it does not see the DMA.)
     s16x4 bcur[8];
+    {
+      float* qw = qbuf + wave * GC * kMfmaUnitCols;
+      const uint32_t qs = (uint32_t)reinterpret_cast<uintptr_t>(qw);
+      const float* qb = p.q + (size_t)b * d;
+      const int ubeg = ubase, uend = clim;                    // own unit's columns [ubeg, min(ubeg + 256, uend))
+      const i32x4 ro = buffer_desc(qb + ubeg, (uint32_t)max(0, min(kMfmaUnitCols, uend - ubeg)) * 4u);
 #pragma unroll
-    for (int s = 0; s < NST; ++s) issue(s, s);
+      for (int k = 0; k < 4; ++k) dma4(qs + k * 256, ro, 4u * (uint32_t)(64 * k + lane));
+      if (GC == 2) {
+        const int xbeg = (1 - cg) * p.dc + wave * kMfmaUnitCols, xend = min(d, (2 - cg) * p.dc);
+        const i32x4 rx = buffer_desc(qb + (xbeg < d ? xbeg : 0), (uint32_t)max(0, min(kMfmaUnitCols, xend - xbeg)) * 4u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dma4(qs + 1024 + k * 256, rx, 4u * (uint32_t)(64 * k + lane));
+      }
+#pragma unroll
+      for (int s = 0; s < NST; ++s) issue(s, s);
+      wait_vmcnt<NST * LPS>();
+      split_q8(qw + 8 * l32, p.qscale, qoh, qol);
+      split_q8(qw + (GC == 2 ? 256 : 0) + 8 * l32, p.qscale, qxh, qxl);
+    }
     wait_vmcnt<(NST - 1) * LPS>();
     scores(0, S + (gstep & 1) * 256);
     b_operands(0, bcur);
@@ -434,7 +463,7 @@ __device__ __forceinline__ void dma16_sc1(uint32_t lds, const i32x4& rsrc, uint3
       "buffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
       :
       : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
+      : "memory", "m0");
 }
 
 template <int NST>
@@ -596,11 +625,16 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 
     // prologue: ring steps 0..3 landed; the own heads' scores of steps 0..2
     // published and the partner's of step 0 in S; B operands of step 0;
-    // step 4 in flight.  The wave's 1 KB of q travels by DMA with the first
-    // ring steps, and each step's scores go out as soon as that step has
-    // landed (the waits count only the younger ring loads).
+    // step 4 in flight.  The wave's 1 KB of q travels by DMA (4-byte
+    // elements: q need only be 4-byte aligned) with the first ring steps,
+    // and each step's scores go out as soon as that step has landed (the
+    // waits count only the younger ring loads).
     s16x4 bcur[8];
-    dma16(qbuf_s, buffer_desc(p.q + (size_t)b * d + ubase, kMfmaUnitCols * 4u), 16u * lane);
+    {
+      const i32x4 rq = buffer_desc(p.q + (size_t)b * d + ubase, kMfmaUnitCols * 4u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dma4(qbuf_s + k * 256, rq, 4u * (uint32_t)(64 * k + lane));
+    }
 #pragma unroll
     for (int s = 0; s < NST; ++s) issue(s);
     wait_vmcnt<NST * LPS>();
@@ -713,7 +747,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   p.dc = pl.dc;
   p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
-  const size_t lds = (size_t)pl.nw * WB + (512 + 16 + (size_t)a.B + 1) * sizeof(int);
+  const size_t lds = (size_t)pl.nw * WB + (512 + (size_t)pl.nw * GC * kMfmaUnitCols + 16 + (size_t)a.B + 1) * sizeof(int);
   auto kern = attend_bf16_kernel<DH, GC, NST>;
   static std::atomic<int> granted[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), lds, granted);
@@ -735,13 +769,11 @@ static uint32_t next_epoch() {
 }
 
 // Launches the exchange kernel when the shape allows it (two full column
-// groups of dh = 128) and q is 16-byte aligned (it is brought to LDS by
-// 16-byte DMA); returns hipErrorNotSupported otherwise, and the caller falls
-// back.
+// groups of dh = 128); returns hipErrorNotSupported otherwise, and the caller
+// falls back.
 static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = 4;
-  if (!pl.xchg || (reinterpret_cast<uintptr_t>(a.q) & 15u) != 0 || env_int("SLIM_XCHG", 1) == 0)
-    return hipErrorNotSupported;
+  if (!pl.xchg || env_int("SLIM_XCHG", 1) == 0) return hipErrorNotSupported;
   XchgParams xp;
   AttendBf16Params& p = xp.a;
   p.q = a.q;

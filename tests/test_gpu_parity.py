@@ -274,10 +274,10 @@ def test_score_exchange_and_fallback(monkeypatch, xchg):
 
 
 def test_exchange_shape_with_q_4_byte_aligned():
-    """q only 4-byte aligned (a view one float into a buffer).  The exchange
-    kernel reads q by 16-byte DMA, so the launcher takes the general
-    two-column-group kernel for it; the result still matches the oracle and
-    equals, to the bf16 tolerance, the call with an aligned q."""
+    """q only 4-byte aligned (a view one float into a buffer) on the
+    exchange kernel's shape: q reaches LDS by 4-byte DMA, so the result
+    matches the oracle and equals, to the bf16 tolerance, the call with an
+    aligned q."""
     import torch
     import kv_cache_reduction_amd as slim
     cfg = syn.shrink(syn.CONFIGS["c2"], B=3, T_max=700, len_lo=1, len_hi=700)
