@@ -18,6 +18,14 @@
 //          threads' sums combined the same way),
 //          then multiplies by the W_KV rows it holds in registers:
 //            part[rb, b, h, j] = sum_{r in rows} u[r] W_KV[r, h*dh + j].
+//          With bf16 W_KV and at least 4 sequences per workgroup this
+//          product runs on MFMA (16x16x16, the workgroup's sequences as the
+//          16 rows of A; with fewer, the padding rows would dominate and
+//          the vector ALU is faster): the W_KV rows go
+//          through LDS in rounds of 64 and reach the B operand by transposing
+//          reads; each merged value is split exactly into three bf16 parts
+//          (u = hi + mid + lo), so the products are exact and only the fp32
+//          accumulation rounds.  fp32 W_KV uses the vector ALU.
 //          The partials are read once and W_KV once per S sequences.
 // reduce   out[b, h, j] = sum_rb part[rb, b, h, j] in a fixed order, so the
 //          result does not depend on scheduling.
@@ -28,8 +36,22 @@
 namespace slim {
 
 constexpr int kMergeBatch = 4;  // slots whose loads a thread issues together
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int DH, bool WBF16, int PR>
+// x = hi + mid + lo exactly, each a bf16 (its bits in the low 16 bits of the
+// result): every part is the remaining value truncated to bf16, and what is
+// left after two parts has at most 8 significant bits.
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t hb = __float_as_uint(x) & 0xffff0000u;
+  const float r = x - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r) & 0xffff0000u;
+  const float r2 = r - __uint_as_float(mb);
+  hi = hb >> 16;
+  mid = mb >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+template <int DH, bool WBF16, int PR, bool MFMA>
 __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __restrict__ lengths,
                                                             const float* __restrict__ U,
                                                             const float* __restrict__ ml,
@@ -49,13 +71,20 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   constexpr int C4 = PR / 4;
   constexpr int NSS = 256 / C4;
   static_assert(C4 * NSS == 256, "merge split");
+  // MFMA projection (bf16 W_KV): W_KV rows through LDS, CR at a time
+  constexpr bool MP = MFMA && WBF16 && DH >= 16 && DH % 16 == 0 && JW == 8;
+  constexpr int CR = PR < 64 ? PR : 64;
+  constexpr int PITCH = DH * 2 + 32;  // bytes per W_KV row in LDS (rows of a transposing read on distinct banks)
+  constexpr int WL = MP ? CR * PITCH / 4 : 0;
+  static_assert(!MP || (CR % 16 == 0 && CR % RPT == 0 && PR % CR == 0), "projection rounds");
   extern __shared__ int smem[];
   int* tmp = smem;                                       // [8]
   float* red = reinterpret_cast<float*>(smem + 8);       // [max(NSS * PR, NRS * DH)]
   constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
   float* us = red + RED;                                 // [spw][PR]
   float* mstar = us + spw * PR;                          // [NSS][2]: running max, normaliser
-  int* pre = reinterpret_cast<int*>(mstar + 2 * NSS);    // [B + 1]
+  char* wl = reinterpret_cast<char*>(mstar + 2 * NSS);   // [CR][PITCH] bytes: W_KV rows of a round (MP)
+  int* pre = reinterpret_cast<int*>(mstar + 2 * NSS + WL);  // [B + 1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, r0 = blockIdx.y * PR, b0 = blockIdx.z * spw;
@@ -65,13 +94,18 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
   // are unconditional (rows past the block clamped, then zeroed) so that
   // they are all in flight together.
   const int jq = tid % JQ, rs = tid / JQ;
-  float w[RPT][JW];
+  float w[MP ? 1 : RPT][JW];  // vector-ALU projection: fp32 values
+  uint4 wq[MP ? RPT : 1];     // MFMA projection: 8 packed bf16 per row
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rs * RPT + i;
     const bool live = r < nr;
     const size_t base = (size_t)(r0 + (live ? r : nr - 1)) * d + (size_t)h * DH + jq * JW;
-    if constexpr (WBF16 && JW == 8) {
+    if constexpr (MP) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + base);
+      wq[i] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    } else if constexpr (WBF16 && JW == 8) {
       const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + base);
       w[i][0] = bf_lo(v.x); w[i][1] = bf_hi(v.x); w[i][2] = bf_lo(v.y); w[i][3] = bf_hi(v.y);
       w[i][4] = bf_lo(v.z); w[i][5] = bf_hi(v.z); w[i][6] = bf_lo(v.w); w[i][7] = bf_hi(v.w);
@@ -82,8 +116,10 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
         else w[i][k] = static_cast<const float*>(W)[base + k];
       }
     }
+    if constexpr (!MP) {
 #pragma unroll
-    for (int k = 0; k < JW; ++k) w[i][k] = live ? w[i][k] : 0.f;
+      for (int k = 0; k < JW; ++k) w[i][k] = live ? w[i][k] : 0.f;
+    }
   }
 
   // slots of sequence b: the chunks its rows fall in (decode), or a fixed
@@ -199,8 +235,67 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
     __syncthreads();
   }
 
-  // projection of each merged row block by the W_KV rows held in registers
   const size_t nout = (size_t)B * H * DH;
+  if constexpr (MP) {
+    // D[m][n] = sum_k u[m][k] W[k][n] over this block's rows: m = sequence
+    // (16 rows of A, those past nb zero), n = 16-column tile of the head.
+    // Lane (g, j) = (lane / 16, lane % 16) holds A[j][4g..4g+3],
+    // B[4g..4g+3][j] and D[4g..4g+3][j].
+    constexpr int NT = DH / 16;
+    constexpr int TPW = NT >= 4 ? NT / 4 : 1;  // tiles per wave
+    const int g = lane >> 4, j = lane & 15;
+    const uint32_t wl_s = (uint32_t)reinterpret_cast<uintptr_t>(wl);
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < PR / CR; ++c) {
+      const int rr = rs * RPT - c * CR;  // this thread's rows, relative to the round
+      if (rr >= 0 && rr < CR) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) *reinterpret_cast<uint4*>(wl + (rr + i) * PITCH + jq * 16) = wq[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < CR / 16; ++ks) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < nb) x = *reinterpret_cast<const float4*>(us + j * PR + c * CR + ks * 16 + 4 * g);
+        uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+        split3_bf16(x.x, h0, m0, l0);
+        split3_bf16(x.y, h1, m1, l1);
+        split3_bf16(x.z, h2, m2, l2);
+        split3_bf16(x.w, h3, m3, l3);
+        const s16x4 ah = {(short)h0, (short)h1, (short)h2, (short)h3};
+        const s16x4 am = {(short)m0, (short)m1, (short)m2, (short)m3};
+        const s16x4 al = {(short)l0, (short)l1, (short)l2, (short)l3};
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const int nt = wave * TPW + t;
+          if (nt < NT) {
+            const lds_s16x4* bp = (const lds_s16x4*)(size_t)(
+                wl_s + (uint32_t)((ks * 16 + 4 * g + (j >> 2)) * PITCH + (nt * 16 + 4 * (j & 3)) * 2));
+            const s16x4 bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(bp));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bv, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(am, bv, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bv, acc[t], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int nt = wave * TPW + t;
+      if (nt < NT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * g + i;
+          if (m < nb) part[(size_t)blockIdx.y * nout + ((size_t)(b0 + m) * H + h) * DH + nt * 16 + j] = acc[t][i];
+        }
+      }
+    }
+    return;
+  }
+  // projection of each merged row block by the W_KV rows held in registers
   for (int bb = 0; bb < nb; ++bb) {
     float acc[JW];
 #pragma unroll
@@ -249,10 +344,19 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
   const int spw = pl.spw == 16 ? 16 : 8;
-  const size_t lds = (8 + (size_t)RED + (size_t)spw * PR + 2 * NSS + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
-  hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR>),
-                     dim3(a.H, pl.npc, (a.B + spw - 1) / spw), dim3(256), lds, s, a.lengths,
-                     U, ml, a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+  // MFMA projection when a workgroup has at least 4 sequences
+  constexpr bool MFMA_OK = WBF16 && DH >= 16 && DH % 16 == 0;
+  const bool mp = MFMA_OK && (a.B < spw ? a.B : spw) >= 4;
+  const int WL = mp ? (PR < 64 ? PR : 64) * (DH * 2 + 32) / 4 : 0;
+  const size_t lds =
+      (8 + (size_t)RED + (size_t)spw * PR + 2 * NSS + WL + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
+  const dim3 grid(a.H, pl.npc, (a.B + spw - 1) / spw);
+  if (mp)
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, MFMA_OK>), grid, dim3(256), lds, s, a.lengths, U, ml,
+                       a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+  else
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false>), grid, dim3(256), lds, s, a.lengths, U, ml,
+                       a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;
