@@ -124,6 +124,11 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
  * Errors: SLIM_ERR_INVALID (null pointers, B/H/dh/T_max <= 0, scale not
  * finite, misaligned pointers), SLIM_ERR_UNSUPPORTED, SLIM_ERR_WORKSPACE,
  * SLIM_ERR_HIP.
+ * Environment (testing): SLIM_CHUNKS=n fixes the number of token chunks the
+ * attend phase cuts the rows into (the workspace size follows it, so query
+ * slim_decode_workspace_bytes with the same setting); SLIM_XCHG=0 turns off
+ * the score-exchange kernel of the d = 4096, dh = 128 shapes.  Results agree
+ * to rounding with the defaults.
  */
 slim_status_t slim_decode(const float* q,
                           const void* K_cache, slim_dtype_t k_dt,
