@@ -296,3 +296,22 @@ def test_exchange_shape_with_q_4_byte_aligned():
     _check("q at a 4-byte offset", o, ref, TOL["bf16"])
     o16 = gpu_decode(cfg, wl.q, Kd, wl.lengths, Wd)
     assert oracle.err_rel(o, o16) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("H,dh,B,T", [(20, 64, 4, 150), (20, 64, 19, 150), (32, 128, 17, 96), (32, 32, 6, 200)])
+def test_finish_mfma_projection_group_tails(H, dh, B, T):
+    """The finish's W_KV projection on MFMA (bf16 W_KV, at least 4 sequences
+    per workgroup): B = 4 at the threshold, a last sequence group of 3
+    (B = 19, 8 per group) and of 1 (B = 17 at d = 4096, 16 per group), and
+    dh = 32 (two 16-column tiles, only two of the four waves hold tiles);
+    ragged lengths with an empty sequence."""
+    cfg = syn.Config(f"tails-{B}", d=H * dh, H=H, dh=dh, B=B, T_max=T, len_lo=1, len_hi=T,
+                     cache="bf16", wkv="bf16", seed=700 + B)
+    wl = syn.make(cfg, with_cache=False)
+    lens = wl.lengths.copy()
+    lens[B // 2] = 0
+    K = syn.k_cache(cfg, wl.w, np.minimum(lens, cfg.T_max))
+    o = gpu_decode(cfg, wl.q, to_dev(K), lens, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
+    assert np.all(o[B // 2] == 0)
+    _check(f"MFMA projection tails H={H} dh={dh} B={B}", o, ref, TOL["bf16"])
