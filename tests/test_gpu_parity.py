@@ -315,3 +315,19 @@ def test_finish_mfma_projection_group_tails(H, dh, B, T):
     ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
     assert np.all(o[B // 2] == 0)
     _check(f"MFMA projection tails H={H} dh={dh} B={B}", o, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("H,dh", [(6, 16), (3, 256)])
+def test_finish_mfma_projection_f32_cache_bf16_wkv(H, dh):
+    """fp32 cache with bf16 W_KV at head widths the bf16-cache path does not
+    take: dh = 16 (one 16-column tile, one wave holds it) and dh = 256
+    (64-row blocks, four tiles per wave), with 5 sequences so that the
+    projection runs on MFMA.  W_KV in bf16 bounds the error, so the bf16
+    tolerance applies."""
+    cfg = syn.Config(f"f32c-bf16w-{dh}", d=H * dh, H=H, dh=dh, B=5, T_max=90, len_lo=1, len_hi=90,
+                     cache="f32", wkv="bf16", seed=900 + dh)
+    wl = syn.make(cfg, with_cache=False)
+    K = syn.k_cache(cfg, wl.w, np.minimum(wl.lengths, cfg.T_max))
+    o = gpu_decode(cfg, wl.q, to_dev(K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    ref = oracle_decode(cfg, wl.q, K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check(f"f32 cache, bf16 W_KV, dh={dh}", o, ref, TOL["bf16"])
