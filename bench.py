@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c2_8k", "c3", "c4"])
+    ap.add_argument("--config", default="long_128k", choices=["gpt2_small", "7b_ragged", "7b_8k", "long_128k", "whisper_large"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip comparator, T=8K point, probe")
     return ap.parse_args()
@@ -228,7 +228,7 @@ def time_multi(torch, slim, steps):
     Device time per call by graph replay."""
     import synthetic as syn
     out = {}
-    cases = [("shared_context", syn.CONFIGS["c4"], 64, False), ("prompt", syn.CONFIGS["c1"], 2048, True)]
+    cases = [("shared_context", syn.CONFIGS["whisper_large"], 64, False), ("prompt", syn.CONFIGS["gpt2_small"], 2048, True)]
     for name, cfg, n, causal in cases:
         w = syn.weights(cfg)
         T = cfg.T_max
@@ -301,7 +301,7 @@ def measured_traffic(kernel_sources):
     """HBM bytes per attend launch from the committed counter summary, if the
     counters were taken on the current kernel source; otherwise None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attend_bf16_c3_counters.json")
+    path = os.path.join(ROOT, "profiles", "attend_bf16_long_128k_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -434,7 +434,7 @@ def main():
         "k_cache_hbm_frac": k_gbps_step / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": k_gbps_attend, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": k_gbps_attend / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(ATTEND_SOURCES) if name == "c3" else None,
+                     "traffic": measured_traffic(ATTEND_SOURCES) if name == "long_128k" else None,
                      "kernel": attend_kernel_name(cfg), "kernel_us": att_ms * 1e3,
                      "algorithmic_bytes": wl.k_bytes},
     }
@@ -463,13 +463,13 @@ def main():
         log(f"[bench] HBM copy probe (read+write): {res['probe_copy_gbps']:.0f} GB/s")
         del wl
         torch.cuda.empty_cache()
-        if name == "c3":
-            w2 = Workload("c2_8k", torch, slim, with_v=False)
+        if name == "long_128k":
+            w2 = Workload("7b_8k", torch, slim, with_v=False)
             ms2, att2 = time_slim(w2, torch, slim, max(10, args.steps // 2), 3)
             res["secondary"] = {"workload": w2.cfg.desc, "tokens_s": w2.cfg.B / (ms2 * 1e-3),
                                 "ms_per_step": ms2, "k_cache_gbps": w2.k_bytes / (ms2 * 1e-3) / 1e9,
                                 "attend_gbps": w2.k_bytes / (att2.mean() * 1e-3) / 1e9}
-            log(f"[bench] c2_8k: {ms2 * 1e3:.1f} us/step, {res['secondary']['k_cache_gbps']:.0f} GB/s")
+            log(f"[bench] 7b_8k: {ms2 * 1e3:.1f} us/step, {res['secondary']['k_cache_gbps']:.0f} GB/s")
             del w2
             torch.cuda.empty_cache()
 

@@ -69,22 +69,22 @@ class Config:
 
 
 CONFIGS = {
-    "c0": Config("c0", d=64, H=4, dh=16, B=1, T_max=32, len_lo=32, len_hi=32,
+    "tiny_f32": Config("tiny_f32", d=64, H=4, dh=16, B=1, T_max=32, len_lo=32, len_hi=32,
                  cache="f32", wkv="f32", seed=0,
                  desc="tiny MHA decode, fp32: d=64 H=4 dh=16 B=1 T=32"),
-    "c1": Config("c1", d=768, H=12, dh=64, B=8, T_max=2048, len_lo=2048, len_hi=2048,
+    "gpt2_small": Config("gpt2_small", d=768, H=12, dh=64, B=8, T_max=2048, len_lo=2048, len_hi=2048,
                  cache="bf16", wkv="bf16", seed=1,
                  desc="GPT-2-small-shaped layer decode: d=768 H=12 dh=64 B=8 T=2048, bf16 K"),
-    "c2": Config("c2", d=4096, H=32, dh=128, B=16, T_max=8192, len_lo=1024, len_hi=8192,
+    "7b_ragged": Config("7b_ragged", d=4096, H=32, dh=128, B=16, T_max=8192, len_lo=1024, len_hi=8192,
                  cache="bf16", wkv="bf16", seed=2,
                  desc="7B-shaped layer decode: d=4096 H=32 dh=128 B=16 T~U[1024,8192], bf16 K and W_KV"),
-    "c2_8k": Config("c2_8k", d=4096, H=32, dh=128, B=16, T_max=8192, len_lo=8192, len_hi=8192,
+    "7b_8k": Config("7b_8k", d=4096, H=32, dh=128, B=16, T_max=8192, len_lo=8192, len_hi=8192,
                     cache="bf16", wkv="bf16", seed=2,
                     desc="7B-shaped layer decode at uniform T=8192: d=4096 H=32 dh=128 B=16"),
-    "c3": Config("c3", d=4096, H=32, dh=128, B=1, T_max=131072, len_lo=131072, len_hi=131072,
+    "long_128k": Config("long_128k", d=4096, H=32, dh=128, B=1, T_max=131072, len_lo=131072, len_hi=131072,
                  cache="bf16", wkv="bf16", seed=3,
                  desc="long-context single-stream decode: d=4096 H=32 dh=128 B=1 T=131072, bf16 K"),
-    "c4": Config("c4", d=1280, H=20, dh=64, B=64, T_max=1500, len_lo=1500, len_hi=1500,
+    "whisper_large": Config("whisper_large", d=1280, H=20, dh=64, B=64, T_max=1500, len_lo=1500, len_hi=1500,
                  cache="bf16", wkv="bf16", seed=4, prefill=True, weights_bf16=True,
                  desc="Whisper-large-shaped cross-attention decode: d=1280 H=20 dh=64 B=64 "
                       "encoder T=1500 written by prefill from X, bf16"),

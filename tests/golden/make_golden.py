@@ -1,5 +1,5 @@
-"""Writes tests/golden/c0_oracle.json: the float64 oracle's output on the
-seeded c0 workload (d=64, H=4, dh=16, B=1, T=32, fp32 cache).
+"""Writes tests/golden/tiny_f32_oracle.json: the float64 oracle's output on the
+seeded tiny_f32 workload (d=64, H=4, dh=16, B=1, T=32, fp32 cache).
 
 It calls only ``oracle`` and ``synthetic``; nothing here touches the HIP
 library.  Rerun after a deliberate change to the oracle or the generator:
@@ -17,19 +17,19 @@ import synthetic as syn  # noqa: E402
 
 
 def main():
-    cfg = syn.CONFIGS["c0"]
+    cfg = syn.CONFIGS["tiny_f32"]
     wl = syn.make(cfg)
     K = oracle.cache_to_f64(wl.K)
     V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
     o = oracle.mha_decode(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
     out = {
-        "what": "float64 oracle output o[B,H,dh] for the seeded c0 workload",
+        "what": "float64 oracle output o[B,H,dh] for the seeded tiny_f32 workload",
         "config": cfg.desc,
         "seed": cfg.seed,
         "writer": "tests/golden/make_golden.py (calls oracle/ and synthetic/ only)",
         "o": o.tolist(),
     }
-    with open(os.path.join(HERE, "c0_oracle.json"), "w") as f:
+    with open(os.path.join(HERE, "tiny_f32_oracle.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
 

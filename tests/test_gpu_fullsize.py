@@ -19,34 +19,34 @@ def _check(name, o, ref):
     assert err <= TOL["bf16"]
 
 
-def test_c2_full_ragged_sampled():
-    cfg = syn.CONFIGS["c2"]
-    log(f"[fullsize] c2: generating {cfg.desc}")
+def test_7b_ragged_full_size_sampled():
+    cfg = syn.CONFIGS["7b_ragged"]
+    log(f"[fullsize] 7b_ragged: generating {cfg.desc}")
     wl = syn.make(cfg)
-    log(f"[fullsize] c2 lengths: {wl.lengths.tolist()}")
+    log(f"[fullsize] 7b_ragged lengths: {wl.lengths.tolist()}")
     o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
     assert np.isfinite(o).all()
     seqs, heads = [0, 7, 15], [0, 13, 31]
     ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V, seqs=seqs, heads=heads)
-    _check("c2", o[np.ix_(seqs, heads)], ref)
+    _check("7b_ragged", o[np.ix_(seqs, heads)], ref)
 
 
-def test_c3_full_131072_sampled_heads():
-    cfg = syn.CONFIGS["c3"]
-    log(f"[fullsize] c3: generating {cfg.desc}")
+def test_long_128k_full_131072_sampled_heads():
+    cfg = syn.CONFIGS["long_128k"]
+    log(f"[fullsize] long_128k: generating {cfg.desc}")
     wl = syn.make(cfg)
     o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
     assert np.isfinite(o).all()
     heads = [0, 17, 31]
     ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V, heads=heads, reassociate=True)
-    _check("c3", o[:, heads], ref)
+    _check("long_128k", o[:, heads], ref)
 
 
-def test_c4_full_prefill_and_decode_sampled():
+def test_whisper_large_full_prefill_and_decode_sampled():
     torch = pytest.importorskip("torch")
     import kv_cache_reduction_amd as slim
-    cfg = syn.CONFIGS["c4"]
-    log(f"[fullsize] c4: generating {cfg.desc}")
+    cfg = syn.CONFIGS["whisper_large"]
+    log(f"[fullsize] whisper_large: generating {cfg.desc}")
     wl = syn.make(cfg, with_cache=False)
     Xb, Wb = syn.prefill_inputs(cfg, wl.w)
     Kd = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
@@ -60,6 +60,6 @@ def test_c4_full_prefill_and_decode_sampled():
     for b in seqs:
         X64 = oracle.bf16_decode(Xb[b])
         K_ref[b] = oracle.prefill(X64, W64, "bf16")
-        check_prefill_bf16(Kbits[b], X64, W64, f"c4 seq {b}")
+        check_prefill_bf16(Kbits[b], X64, W64, f"whisper_large seq {b}")
     ref = oracle_decode(cfg, wl.q, K_ref, wl.lengths, wl.w.W_K, wl.w.W_V, seqs=seqs)
-    _check("c4", o[seqs], ref)
+    _check("whisper_large", o[seqs], ref)

@@ -50,16 +50,16 @@ def _run(name, cfg, Q, K, Wkv, w, limits, option, tol=TOL["bf16"]):
 
 
 @pytest.mark.parametrize("option", [1, 2])
-def test_shared_context_c4_shape(option):
-    cfg = syn.shrink(syn.CONFIGS["c4"], B=64, T_max=200, len_lo=200, len_hi=200)
+def test_shared_context_whisper_large_shape(option):
+    cfg = syn.shrink(syn.CONFIGS["whisper_large"], B=64, T_max=200, len_lo=200, len_hi=200)
     w, K, Wkv = _context(cfg, 200)
     Q = syn.queries(cfg, w)                       # 64 decoder queries, one encoder context
-    _run("shared c4-shaped", cfg, Q, K, Wkv, w, None, option)
+    _run("shared whisper_large-shaped", cfg, Q, K, Wkv, w, None, option)
 
 
 @pytest.mark.parametrize("option", [1, 2])
 def test_ragged_limits_dh128(option):
-    cfg = syn.shrink(syn.CONFIGS["c2"], B=40, T_max=300, len_lo=300, len_hi=300)
+    cfg = syn.shrink(syn.CONFIGS["7b_ragged"], B=40, T_max=300, len_lo=300, len_hi=300)
     w, K, Wkv = _context(cfg, 300)
     Q = syn.queries(cfg, w)                       # 40 queries: a ragged last block of 32
     lim = (np.arange(40) * 37) % 331 - 10         # negative, zero, partial tiles, beyond T
@@ -68,19 +68,19 @@ def test_ragged_limits_dh128(option):
 
 @pytest.mark.parametrize("option", [1, 2])
 def test_prompt_phase_causal(option):
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=1, T_max=230, len_lo=230, len_hi=230)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=1, T_max=230, len_lo=230, len_hi=230)
     w, K, Wkv = _context(cfg, 230)
     t0 = 37                                       # the prompt continues a cached prefix
     X = syn.x_rows(cfg, 0, t0, 230).astype(np.float64)
     Q = (X @ w.W_Q).astype(np.float32)
     lim = t0 + np.arange(230 - t0) + 1
-    _run("prompt causal c1-shaped", cfg, Q, K, Wkv, w, lim, option)
+    _run("prompt causal gpt2_small-shaped", cfg, Q, K, Wkv, w, lim, option)
 
 
 def test_options_agree_and_one_query_is_decode():
     import torch
     import kv_cache_reduction_amd as slim
-    cfg = syn.shrink(syn.CONFIGS["c4"], B=3, T_max=161, len_lo=161, len_hi=161)
+    cfg = syn.shrink(syn.CONFIGS["whisper_large"], B=3, T_max=161, len_lo=161, len_hi=161)
     w, K, Wkv = _context(cfg, 161)
     Q = syn.queries(cfg, w)
     o1 = _run("agree", cfg, Q, K, Wkv, w, None, 1)
@@ -95,13 +95,13 @@ def test_options_agree_and_one_query_is_decode():
 
 
 @pytest.mark.parametrize("option", [0, 1, 2])
-def test_c4_full_shared_encoder_context(option):
+def test_whisper_large_full_shared_encoder_context(option):
     """Whisper-large-shaped cross-attention at full size with one shared
     encoder context: 64 decoder queries, T=1500, d=1280, K written by the
     device prefill from bf16 X and W_K."""
     import torch
     import kv_cache_reduction_amd as slim
-    cfg = syn.CONFIGS["c4"]
+    cfg = syn.CONFIGS["whisper_large"]
     w = syn.weights(cfg)
     Xb, Wb = syn.prefill_inputs(syn.shrink(cfg, B=1), w)
     Kd = torch.zeros((1, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
@@ -109,10 +109,10 @@ def test_c4_full_shared_encoder_context(option):
     torch.cuda.synchronize()
     K = bf16_bits(Kd)[0]
     X64, W64 = oracle.bf16_decode(Xb[0]), oracle.bf16_decode(Wb)
-    check_prefill_bf16(K, X64, W64, "c4 shared context")
+    check_prefill_bf16(K, X64, W64, "whisper_large shared context")
     Wkv = to_dev(slim.wkv(w.W_K, w.W_V, cfg.wkv))
     Q = syn.queries(cfg, w)
-    _run("c4 full shared context", cfg, Q, K, Wkv, w, None, option)
+    _run("whisper_large full shared context", cfg, Q, K, Wkv, w, None, option)
 
 
 def test_rejects_bad_arguments():
@@ -135,14 +135,14 @@ def test_rejects_bad_arguments():
 def test_small_contexts_and_query_counts(T, n, option):
     """Contexts shorter than one tile, a single query, query counts that
     leave partial query blocks, in both options."""
-    cfg = syn.shrink(syn.CONFIGS["c4"], B=n, T_max=T, len_lo=T, len_hi=T)
+    cfg = syn.shrink(syn.CONFIGS["whisper_large"], B=n, T_max=T, len_lo=T, len_hi=T)
     w, K, Wkv = _context(cfg, T)
     Q = syn.queries(cfg, w)
     _run(f"small T={T} n={n}", cfg, Q, K, Wkv, w, None, option)
 
 
 def test_all_limits_zero_gives_zeros():
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=9, T_max=40, len_lo=40, len_hi=40)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=9, T_max=40, len_lo=40, len_hi=40)
     w, K, Wkv = _context(cfg, 40)
     Q = syn.queries(cfg, w)
     for option in (1, 2):

@@ -94,37 +94,37 @@ def _run_case(name, cfg, lens, T_alloc=None, seed_shift=0):
     return o
 
 
-def test_step_c0_fp32():
-    cfg = syn.CONFIGS["c0"]
-    _run_case("c0", cfg, [20])
+def test_step_tiny_f32():
+    cfg = syn.CONFIGS["tiny_f32"]
+    _run_case("tiny_f32", cfg, [20])
 
 
-def test_step_c0_fp32_full_and_empty():
-    cfg = syn.shrink(syn.CONFIGS["c0"], B=3, T_max=32)
-    _run_case("c0 full/empty", cfg, [32, 0, 31])
+def test_step_tiny_f32_full_and_empty():
+    cfg = syn.shrink(syn.CONFIGS["tiny_f32"], B=3, T_max=32)
+    _run_case("tiny_f32 full/empty", cfg, [32, 0, 31])
 
 
-def test_step_c1_shape_ragged():
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=6, T_max=200, len_lo=0, len_hi=200)
-    _run_case("c1-shaped", cfg, [0, 1, 200, 77, 150, 199])
+def test_step_gpt2_small_shape_ragged():
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=6, T_max=200, len_lo=0, len_hi=200)
+    _run_case("gpt2_small-shaped", cfg, [0, 1, 200, 77, 150, 199])
 
 
-def test_step_c2_shape_two_column_groups():
-    cfg = syn.shrink(syn.CONFIGS["c2"], B=3, T_max=300, len_lo=0, len_hi=300)
-    _run_case("c2-shaped", cfg, [300, 129, 0])
+def test_step_7b_ragged_shape_two_column_groups():
+    cfg = syn.shrink(syn.CONFIGS["7b_ragged"], B=3, T_max=300, len_lo=0, len_hi=300)
+    _run_case("7b_ragged-shaped", cfg, [300, 129, 0])
 
 
-def test_step_c4_shape_two_sequence_groups():
+def test_step_whisper_large_shape_two_sequence_groups():
     # B = 20: the projection handles 16 sequences per workgroup, so two groups
-    cfg = syn.shrink(syn.CONFIGS["c4"], B=20, T_max=64, len_lo=0, len_hi=64)
+    cfg = syn.shrink(syn.CONFIGS["whisper_large"], B=20, T_max=64, len_lo=0, len_hi=64)
     lens = (np.arange(20) * 7) % 65
-    _run_case("c4-shaped", cfg, lens)
+    _run_case("whisper_large-shaped", cfg, lens)
 
 
 def test_step_two_steps_alternating_lengths():
     import torch
     import kv_cache_reduction_amd as slim
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=3, T_max=96, len_lo=0, len_hi=96)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=3, T_max=96, len_lo=0, len_hi=96)
     w = syn.weights(cfg)
     lens0 = np.array([5, 95, 0], dtype=np.int32)
     K = syn.k_cache(cfg, w, lens0)
@@ -162,7 +162,7 @@ def test_step_two_steps_alternating_lengths():
 def test_step_rejects_aliased_lengths():
     import torch
     import kv_cache_reduction_amd as slim
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=2, T_max=16)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=2, T_max=16)
     w = syn.weights(cfg)
     WQd, WKd, _, _, Wkv = _weights_dev(cfg, w)
     Kd = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
@@ -173,15 +173,15 @@ def test_step_rejects_aliased_lengths():
         slim.step(x, WQd, WKd, Kd, ld, ld, Wkv, out, cfg.H, cfg.dh, cfg.scale)
 
 
-def test_step_c3_full_size_sampled_heads():
+def test_step_long_128k_full_size_sampled_heads():
     """The long-context step at its real size: 131071 cached rows of d=4096,
     the new row lands at 131071.  Sampled heads against the oracle, the
     appended row in full."""
-    cfg = syn.CONFIGS["c3"]
+    cfg = syn.CONFIGS["long_128k"]
     w = syn.weights(cfg)
     T = cfg.T_max
     lens = np.array([T - 1], dtype=np.int32)
-    log(f"[step] c3 full size: generating {T - 1} rows")
+    log(f"[step] long_128k full size: generating {T - 1} rows")
     K = syn.k_cache(cfg, w, lens)
     x = syn.x_new(cfg)
     WQd, WKd, WQ64, WK64, Wkv = _weights_dev(cfg, w)
@@ -193,15 +193,15 @@ def test_step_c3_full_size_sampled_heads():
     heads = [0, 21, 31]
     ref = oracle_decode(cfg, q, K, lens, WK64, w.W_V, heads=heads, reassociate=True)
     err = oracle.err_rel(o[:, heads], ref)
-    log(f"[step] c3 full size: err={err:.3e}")
+    log(f"[step] long_128k full size: err={err:.3e}")
     assert err <= TOL["bf16"]
     got = bf16_bits(Kd[:, T - 1])
-    check_prefill_bf16(got, x.astype(np.float64), WK64, "c3 appended row")
+    check_prefill_bf16(got, x.astype(np.float64), WK64, "long_128k appended row")
 
 
 def test_step_one_row_cache_and_many_sequences():
     """T_max = 1 (the first step fills the cache, the next finds it full) and
     B = 100 (seven projection groups of 16 sequences, a ragged last one)."""
-    cfg = syn.shrink(syn.CONFIGS["c1"], B=100, T_max=1, len_lo=0, len_hi=1)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], B=100, T_max=1, len_lo=0, len_hi=1)
     lens = (np.arange(100) % 2).astype(np.int32)        # empty and full caches
     _run_case("T_max=1 B=100", cfg, lens)

@@ -74,7 +74,7 @@ def test_hand_wkv_and_prefill():
 # ---------------------------------------------------------------------------
 # closed forms and the rewrite identity
 
-@pytest.mark.parametrize("name", ["c0", "c1"])
+@pytest.mark.parametrize("name", ["tiny_f32", "gpt2_small"])
 def test_wkv_closed_form(name):
     """W_K = Qo diag(s) Ro  =>  W_K^-1 = Ro^T diag(1/s) Qo^T, so
     W_KV = Ro^T diag(1/s) Qo^T W_V exactly."""
@@ -84,10 +84,10 @@ def test_wkv_closed_form(name):
     assert _rel(oracle.wkv(w.W_K, w.W_V), closed) < 1e-12
 
 
-def test_eq2_rewrite_c0():
+def test_eq2_rewrite_tiny_f32():
     """V = X.W_V = (X.W_K).W_KV in float64 to 1e-10 (the identity of the
     article's "K-Cache is All You Need" section)."""
-    cfg = syn.CONFIGS["c0"]
+    cfg = syn.CONFIGS["tiny_f32"]
     w = syn.weights(cfg)
     X = syn.x_rows(cfg, 0, 0, cfg.T_max).astype(np.float64)
     V = X @ w.W_V
@@ -95,10 +95,10 @@ def test_eq2_rewrite_c0():
     assert _rel(V2, V) < 1e-10
 
 
-def test_explicit_values_matches_unrounded_mha_c0():
+def test_explicit_values_matches_unrounded_mha_tiny_f32():
     """For an fp32 cache, X~ = K~ W_K^-1 recovers X to fp32 rounding and the
     explicit V tracks X.W_V to the same order."""
-    cfg = syn.CONFIGS["c0"]
+    cfg = syn.CONFIGS["tiny_f32"]
     w = syn.weights(cfg)
     lens = syn.lengths(cfg)
     K = syn.k_cache(cfg, w, lens)
@@ -108,7 +108,7 @@ def test_explicit_values_matches_unrounded_mha_c0():
 
 
 def test_explicit_values_cols_matches_full():
-    cfg = syn.shrink(syn.CONFIGS["c1"], T_max=96, B=2)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], T_max=96, B=2)
     wl = syn.make(cfg)
     cols = np.r_[64:128, 640:704]
     full = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)[..., cols]
@@ -127,8 +127,8 @@ def test_loop_vs_matrix(seed, T, H, dh):
     assert _rel(a, b) < 1e-12
 
 
-def test_loop_vs_matrix_c0():
-    cfg = syn.CONFIGS["c0"]
+def test_loop_vs_matrix_tiny_f32():
+    cfg = syn.CONFIGS["tiny_f32"]
     wl = syn.make(cfg)
     K = oracle.cache_to_f64(wl.K)
     V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
@@ -211,7 +211,7 @@ def test_identity_wk_gives_wv():
 # ---------------------------------------------------------------------------
 # the Slim forms agree with explicit-V MHA
 
-@pytest.mark.parametrize("name,T,B", [("c0", None, None), ("c1", 64, 2)])
+@pytest.mark.parametrize("name,T,B", [("tiny_f32", None, None), ("gpt2_small", 64, 2)])
 def test_opt1_opt2_explicit_agree(name, T, B):
     cfg = syn.CONFIGS[name]
     if T is not None:
@@ -247,7 +247,7 @@ def test_round_bf16_matches_torch():
 
 
 def test_generator_row_blocks_are_stable():
-    cfg = syn.shrink(syn.CONFIGS["c1"], T_max=3000, B=1)
+    cfg = syn.shrink(syn.CONFIGS["gpt2_small"], T_max=3000, B=1)
     a = syn.x_rows(cfg, 0, 0, 3000)
     b = syn.x_rows(cfg, 0, 500, 2100)
     c = syn.x_rows(cfg, 0, 0, 700)
@@ -256,7 +256,7 @@ def test_generator_row_blocks_are_stable():
 
 
 def test_generator_wk_conditioning():
-    for name in ("c0", "c1", "c4"):
+    for name in ("tiny_f32", "gpt2_small", "whisper_large"):
         w = syn.weights(syn.CONFIGS[name])
         assert np.linalg.cond(w.W_K) <= 4.0 * 1.01
 
@@ -271,11 +271,11 @@ def test_memory_halving():
         assert k_only * 2 == kv
 
 
-def test_golden_c0_regression():
+def test_golden_tiny_f32_regression():
     """Guards the oracle against drift: output written by
     tests/golden/make_golden.py (which calls only oracle/ and synthetic/)."""
-    g = _load("c0_oracle.json")
-    cfg = syn.CONFIGS["c0"]
+    g = _load("tiny_f32_oracle.json")
+    cfg = syn.CONFIGS["tiny_f32"]
     wl = syn.make(cfg)
     K = oracle.cache_to_f64(wl.K)
     V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)
