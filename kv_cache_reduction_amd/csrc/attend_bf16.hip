@@ -430,17 +430,19 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
 // within a few steps of each other).  A reader thus tells a fresh entry from
 // an old one without any ordering between entries (relaxed agent-scope
 // atomics: no fences, no drain of the DMA queue).  In step i a wave
-//   1. checks the partner's entries of step i+1 (loaded by LDS DMA during
-//      step i-1) and copies them into the score buffer,
-//   2. starts the load of the partner's entries of step i+2,
-//   3. forms and publishes its own heads' scores of step i+3,
-//   4. reads the MFMA B operands of step i+1 and refills that ring slot with
+//   1. starts the load (LDS DMA) of the partner's entries of step i+1,
+//   2. forms and publishes its own heads' scores of step i+3,
+//   3. reads the MFMA B operands of step i+1 and refills that ring slot with
 //      step i+5,
-//   5. runs the softmax and MFMAs of step i,
-// then the workgroup meets at a barrier.  Each wave's vector-memory queue
-// then holds, in order: poll(i+2), publish(i+3), 4 loads of step i+5, so
-// vmcnt(5) at the top of step i+1 means poll(i+2) has landed (and with it
-// the older ring loads).  A late partner is waited for with a bounded spin;
+//   4. runs the softmax and MFMAs of step i,
+//   5. waits for the load of step 1 and copies the partner's entries of step
+//      i+1 into the score buffer,
+// then the workgroup meets at a barrier.  At the wait of step 5 the wave's
+// vector-memory queue holds, oldest first: poll(i+1), publish(i+3), the 4
+// loads of step i+5, so vmcnt(5) means poll(i+1) has landed, and with it
+// the older ring loads (step i+4's, which step i+1 publishes from).  The
+// partner published step i+1 two steps earlier.  A late partner is waited
+// for with a bounded spin;
 // running out of it marks the piece's results NaN.  Workgroups take their
 // roles in arrival order (see the kernel), so the two of a pair are
 // resident together without a cooperative launch.
