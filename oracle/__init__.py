@@ -31,6 +31,7 @@ from .mha import (  # noqa: F401
     mha_decode_loop,
     explicit_values,
     explicit_values_cols,
+    value_map,
     wkv,
     slim_decode_opt1,
     slim_decode_opt2,

@@ -129,14 +129,23 @@ def explicit_values(K, W_K, W_V, cols=None, block: int = 8192) -> np.ndarray:
     return out.reshape(shape[:-1] + (Wv.shape[1],))
 
 
-def explicit_values_cols(K, W_K, W_V, cols, block: int = 16384) -> np.ndarray:
-    """V[..., cols] of ``explicit_values`` for a few columns, with the float64
-    product associated the other way: K~ . (W_K^-1 . W_V[:, cols]) instead of
-    (K~ . W_K^-1) . W_V[:, cols].  Same definition, O(T d |cols|) work instead
-    of O(T d^2); used for sampled heads of very long caches and pinned against
-    ``explicit_values`` on small inputs."""
+def value_map(W_K, W_V, cols=None) -> np.ndarray:
+    """M = W_K^-1 . W_V[:, cols] by float64 solve of W_K . M = W_V[:, cols]:
+    the map from cache rows to the value columns ``cols`` of the context that
+    produced them (V[:, cols] = K~ . M), for ``explicit_values_cols``."""
+    W_V = np.asarray(W_V, dtype=np.float64)
+    return np.linalg.solve(np.asarray(W_K, dtype=np.float64), W_V if cols is None else W_V[:, cols])
+
+
+def explicit_values_cols(K, W_K, W_V, cols, block: int = 16384, M=None) -> np.ndarray:
+    """V[..., cols] of ``explicit_values``, with the float64 product
+    associated the other way: K~ . (W_K^-1 . W_V[:, cols]) instead of
+    (K~ . W_K^-1) . W_V[:, cols].  Same definition, one d x d solve instead of
+    one per row block; used for the full-size caches and pinned against
+    ``explicit_values`` on small inputs.  ``M`` may pass ``value_map(W_K, W_V,
+    cols)`` computed once for many calls (W_K and W_V are then not used)."""
     K = np.asarray(K)
-    Y = np.linalg.solve(np.asarray(W_K, dtype=np.float64), np.asarray(W_V, dtype=np.float64)[:, cols])
+    Y = value_map(W_K, W_V, cols) if M is None else np.asarray(M, dtype=np.float64)
     shape = K.shape
     flat = K.reshape(-1, shape[-1])
     out = np.empty((flat.shape[0], Y.shape[1]))
@@ -220,7 +229,11 @@ def prefill_loop(X, W_K, cache: str) -> np.ndarray:
 
 
 def err_rel(o, o_ref) -> float:
-    """max |o - o_ref| / max |o_ref| over the whole output."""
+    """The parity metric: max |o - o_ref| / max |o_ref|, both maxima over the
+    whole output (every sequence, head and column), i.e. the max-abs error
+    relative to the reference output's L-infinity norm.  When the reference
+    is zero everywhere the metric is the absolute max |o - o_ref|.  A NaN
+    anywhere makes the result NaN, which fails every `err <= tol` gate."""
     o = np.asarray(o, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     den = np.abs(o_ref).max()

@@ -114,6 +114,34 @@ def test_explicit_values_cols_matches_full():
     full = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)[..., cols]
     part = oracle.explicit_values_cols(wl.K, wl.w.W_K, wl.w.W_V, cols)
     assert _rel(part, full) < 1e-12
+    once = oracle.explicit_values_cols(wl.K, None, None, cols, M=oracle.value_map(wl.w.W_K, wl.w.W_V)[:, cols])
+    assert _rel(once, full) < 1e-12
+
+
+def test_value_map_closed_form():
+    """value_map = W_K^-1 W_V[:, cols] = Ro^T diag(1/s) Qo^T W_V[:, cols]."""
+    cfg = syn.CONFIGS["gpt2_small"]
+    w = syn.weights(cfg)
+    cols = np.r_[0:64, 700:768]
+    closed = (w.Ro.T / w.s[None, :]) @ (w.Qo.T @ w.W_V[:, cols])
+    assert _rel(oracle.value_map(w.W_K, w.W_V, cols), closed) < 1e-12
+
+
+def test_whole_output_reference_helper():
+    """The head-group-by-head-group reference of the full-size GPU tests
+    equals the plain definition over explicit_values on a ragged case."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from gpu_common import oracle_decode_full
+    cfg = syn.shrink(syn.CONFIGS["7b_ragged"], d=256, H=4, dh=64, B=4, T_max=40, len_lo=0, len_hi=40)
+    wl = syn.make(cfg)
+    lens = np.array([40, 0, 1, 23], dtype=np.int32)
+    K = syn.k_cache(cfg, wl.w, lens)
+    want = oracle.mha_decode(wl.q, oracle.cache_to_f64(K), oracle.explicit_values(K, wl.w.W_K, wl.w.W_V),
+                             lens, cfg.H, cfg.dh, cfg.scale)
+    got = oracle_decode_full(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V, head_group=3)
+    assert _rel(got, want) < 1e-12
+    assert np.abs(got[1]).max() == 0
 
 
 # ---------------------------------------------------------------------------
@@ -530,7 +558,124 @@ def test_multi_query_cost_model():
     assert c["opt2"] < c["opt1"]
     c = oracle.multi_query_cost(2048, 12, 2048, 768)                 # a whole prompt: option 1
     assert c["opt1"] < c["opt2"]
-    # the crossover for a decode-sized context sits near n ~ d / H queries
-    n_star = next(n for n in range(1, 10000) if (lambda c: c["opt1"] < c["opt2"])(
-        oracle.multi_query_cost(n, 20, 1500, 1280)))
-    assert 40 <= n_star <= 80
+
+
+def test_multi_query_cost_hand_worked():
+    """Exact counts worked by hand (tests/golden/multi_query_cost_worked.json).
+    Every term of both counts is non-zero there, so dropping any one of the
+    four terms changes a value."""
+    for c in _load("multi_query_cost_worked.json")["cases"]:
+        got = oracle.multi_query_cost(c["n"], c["H"], c["T"], c["d"])
+        assert got == {"opt1": c["opt1"], "opt2": c["opt2"]}, c
+
+
+def _counted_options(Q, K, Wkv, H, dh, scale):
+    """Both generation options written as scalar loops that count their
+    multiply-accumulates (the scores, common to both, are not counted).
+    Returns (out1, macs1, out2, macs2)."""
+    n, d = Q.shape
+    T = K.shape[0]
+    p = np.zeros((n, H, T))
+    for i in range(n):
+        for h in range(H):
+            s = np.array([scale * sum(Q[i, h * dh + j] * K[t, h * dh + j] for j in range(dh)) for t in range(T)])
+            e = np.exp(s - s.max())
+            p[i, h] = e / e.sum()
+    macs1 = 0
+    V = np.zeros((T, d))                                   # option 1: V = K . W_KV ...
+    for t in range(T):
+        for c in range(d):
+            for k in range(d):
+                V[t, c] += K[t, k] * Wkv[k, c]
+                macs1 += 1
+    out1 = np.zeros((n, H, dh))                            # ... then softmax times V
+    for i in range(n):
+        for h in range(H):
+            for j in range(dh):
+                for t in range(T):
+                    out1[i, h, j] += p[i, h, t] * V[t, h * dh + j]
+                    macs1 += 1
+    macs2 = 0
+    out2 = np.zeros((n, H, dh))
+    for i in range(n):
+        for h in range(H):
+            u = np.zeros(d)                                # option 2: softmax times all d columns of K ...
+            for c in range(d):
+                for t in range(T):
+                    u[c] += p[i, h, t] * K[t, c]
+                    macs2 += 1
+            for j in range(dh):                            # ... then the head's columns of W_KV
+                for c in range(d):
+                    out2[i, h, j] += u[c] * Wkv[c, h * dh + j]
+                    macs2 += 1
+    return out1, macs1, out2, macs2
+
+
+@pytest.mark.parametrize("n,H,dh,T", [(3, 2, 2, 5), (1, 2, 2, 5), (2, 3, 1, 4)])
+def test_multi_query_cost_counts_the_loops(n, H, dh, T):
+    """The cost model equals the multiply-accumulates that brute-force loops of
+    the two options perform, and those loops reproduce the explicit-V
+    definition (so they are the options, not just counters)."""
+    rng = np.random.default_rng(31 + n + T)
+    d = H * dh
+    Q, K, Wkv = rng.standard_normal((n, d)), rng.standard_normal((T, d)), rng.standard_normal((d, d))
+    out1, m1, out2, m2 = _counted_options(Q, K, Wkv, H, dh, 0.6)
+    want = oracle.multi_query_attention(Q, K, K @ Wkv, None, H, dh, 0.6)
+    assert _rel(out1, want) < 1e-12 and _rel(out2, want) < 1e-12
+    assert oracle.multi_query_cost(n, H, T, d) == {"opt1": m1, "opt2": m2}
+
+
+@pytest.mark.parametrize("drop", range(4))
+def test_multi_query_cost_pin_catches_a_dropped_term(drop):
+    def mutant(n, H, T, d):
+        t = [T * d * d, n * T * d, n * H * T * d, n * d * d]
+        t[drop] = 0
+        return {"opt1": t[0] + t[1], "opt2": t[2] + t[3]}
+    cases = _load("multi_query_cost_worked.json")["cases"]
+    assert any(mutant(c["n"], c["H"], c["T"], c["d"]) != {"opt1": c["opt1"], "opt2": c["opt2"]} for c in cases)
+    _, m1, _, m2 = _counted_options(*(np.ones((3, 4)), np.ones((5, 4)), np.ones((4, 4))), 2, 2, 1.0)
+    assert mutant(3, 2, 5, 4) != {"opt1": m1, "opt2": m2}
+
+
+# ---------------------------------------------------------------------------
+# the parity metric
+
+def test_err_rel_hand_worked():
+    """max|o - o_ref| / max|o_ref| over the whole output, worked by hand
+    (tests/golden/err_rel_worked.json): the error's and the reference's maxima
+    at different indexes, a negative largest difference, 3-D outputs, the
+    all-zero reference (absolute error), and a case where one sequence alone
+    would give a different value."""
+    for c in _load("err_rel_worked.json")["cases"]:
+        assert abs(oracle.err_rel(np.array(c["o"]), np.array(c["o_ref"])) - c["err"]) < 1e-12, c["name"]
+
+
+def test_err_rel_nan_fails_every_gate():
+    o = np.array([[np.nan, 1.0]])
+    assert not (oracle.err_rel(o, np.array([[1.0, 1.0]])) <= 1.0)
+    assert not (oracle.err_rel(np.array([[1.0, 1.0]]), o) <= 1.0)
+
+
+def _err_mutants():
+    a = lambda x: np.asarray(x, dtype=np.float64)
+    return [
+        lambda o, r: float(np.abs(a(o) - a(r)).mean() / np.abs(a(r)).max()),          # mean for max
+        lambda o, r: float((a(o) - a(r)).max() / np.abs(a(r)).max()),                 # no abs on the error
+        lambda o, r: float(np.abs(a(o) - a(r)).max() / a(r).max()),                   # signed max of ref
+        lambda o, r: float(np.abs(a(o) - a(r)).max() / np.abs(a(o)).max()),          # max of o, not ref
+        lambda o, r: float((np.abs(a(o) - a(r)) / np.maximum(np.abs(a(r)), 1e-300)).max()),  # elementwise
+        lambda o, r: max(float(np.abs(a(o)[b] - a(r)[b]).max() / max(np.abs(a(r)[b]).max(), 1e-300))
+                         for b in range(a(r).shape[0])),                               # per sequence
+        lambda o, r: 0.0 if np.abs(a(r)).max() == 0 else float(
+            np.abs(a(o) - a(r)).max() / np.abs(a(r)).max()),                          # zero ref read as exact
+    ]
+
+
+@pytest.mark.parametrize("k", range(7))
+def test_err_rel_pin_catches_planted_mistakes(k):
+    f = _err_mutants()[k]
+    cases = _load("err_rel_worked.json")["cases"]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        bad = [c["name"] for c in cases
+               if not abs(f(np.array(c["o"]), np.array(c["o_ref"])) - c["err"]) < 1e-12]
+    assert bad, "a planted mistake in the metric passed every worked case"
