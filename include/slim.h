@@ -44,7 +44,9 @@ typedef enum {
   SLIM_ERR_UNSUPPORTED = 2,  /* valid but not built (dtype pair, H, dh...) */
   SLIM_ERR_WORKSPACE = 3,    /* workspace_bytes below the required size    */
   SLIM_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
-  SLIM_ERR_SINGULAR = 5      /* W_K is singular to working precision       */
+  SLIM_ERR_SINGULAR = 5,     /* W_K is singular to working precision       */
+  SLIM_ERR_TIMEOUT = 6       /* device side: an attend workgroup gave up
+                                waiting for its partner (slim_decode_status) */
 } slim_status_t;
 
 typedef enum { SLIM_F32 = 0, SLIM_BF16 = 1 } slim_dtype_t;
@@ -124,11 +126,27 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
  * Errors: SLIM_ERR_INVALID (null pointers, B/H/dh/T_max <= 0, scale not
  * finite, misaligned pointers), SLIM_ERR_UNSUPPORTED, SLIM_ERR_WORKSPACE,
  * SLIM_ERR_HIP.
+ * Score exchange (d = 4096-class shapes: bf16, dh = 128, d > 2048, d a
+ * multiple of 512): the two workgroups that share a token chunk swap their
+ * heads' scores through the workspace and wait for each other.  They take
+ * their roles in arrival order, so a partner is always a workgroup that has
+ * already started or is the next to start; the wait assumes that next one
+ * becomes resident while the first waits (true unless other work keeps
+ * almost every compute unit busy for a long time).  Each wait is bounded
+ * (about a second); a workgroup that runs out of it marks its pieces
+ * failed, those sequences' outputs become NaN, and slim_decode_status
+ * reports SLIM_ERR_TIMEOUT.  The call itself returns SLIM_OK (the failure
+ * happens on the device, after the call has returned).
+ * Graph capture: the call may be captured into a HIP graph; while the stream
+ * is capturing, a reset of the exchange's mailboxes is recorded before the
+ * attend so that every replay starts clean.
  * Environment (testing): SLIM_CHUNKS=n fixes the number of token chunks the
  * attend phase cuts the rows into (the workspace size follows it, so query
  * slim_decode_workspace_bytes with the same setting); SLIM_XCHG=0 turns off
- * the score-exchange kernel of the d = 4096, dh = 128 shapes.  Results agree
- * to rounding with the defaults.
+ * the score-exchange kernel.  Results agree to rounding with the defaults.
+ * SLIM_XCHG_SPIN=n bounds each exchange wait to n re-polls, and
+ * SLIM_XCHG_SKEW=1 makes one column group's entries never match, so that
+ * every wait runs out (failure-path tests).
  */
 slim_status_t slim_decode(const float* q,
                           const void* K_cache, slim_dtype_t k_dt,
@@ -138,6 +156,18 @@ slim_status_t slim_decode(const float* q,
                           int B, int H, int dh, int T_max, float scale,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * slim_decode_status -- the device-side outcome of the last slim_decode,
+ * slim_step or attend + finish pair that used `workspace` (the first 256
+ * bytes of a decode or step workspace hold a status word: the attend clears
+ * it and the finish sets it when a piece was marked failed).  Waits for
+ * `stream` (this call synchronises), then returns SLIM_OK or
+ * SLIM_ERR_TIMEOUT (see "Score exchange" above).
+ * Errors: SLIM_ERR_INVALID (null or misaligned workspace, workspace_bytes
+ * < 256), SLIM_ERR_HIP.
+ */
+slim_status_t slim_decode_status(const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * slim_decode_attend / slim_decode_finish -- the two halves of slim_decode,

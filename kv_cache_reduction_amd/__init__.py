@@ -26,7 +26,8 @@ lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration", 3: "workspace too small",
-          4: "HIP runtime error", 5: "W_K is singular"}
+          4: "HIP runtime error", 5: "W_K is singular", 6: "an attend workgroup gave up waiting for its partner"}
+TIMEOUT = 6
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -42,6 +43,8 @@ for _name in ("slim_decode", "slim_decode_attend", "slim_decode_finish"):
     _fn = getattr(lib, _name)
     _fn.restype = _i
     _fn.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+lib.slim_decode_status.restype = _i
+lib.slim_decode_status.argtypes = [_vp, _sz, _vp]
 lib.slim_step_workspace_bytes.restype = _sz
 lib.slim_step_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
 lib.slim_step.restype = _i
@@ -183,6 +186,15 @@ def decode_attend(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, st
 def decode_finish(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, stream=None) -> None:
     _check(lib.slim_decode_finish(*_decode_args(q, K_cache, lengths, W_KV, out, H, dh, scale, ws),
                                   _stream(stream)), "slim_decode_finish")
+
+
+def decode_status(ws, stream=None) -> int:
+    """Device-side outcome of the last decode or step on workspace `ws`
+    (waits for the stream): 0, or TIMEOUT when an exchange wait gave up."""
+    st = int(lib.slim_decode_status(_dev(ws), ws.numel(), _stream(stream)))
+    if st not in (0, TIMEOUT):
+        _check(st, "slim_decode_status")
+    return st
 
 
 def step_workspace_bytes(B: int, H: int, dh: int, T_max: int, k_dtype) -> int:

@@ -77,6 +77,12 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   if (nch < 1) nch = 1;
   const int ov = env_int("SLIM_CHUNKS", 0);
   if (ov > 0) nch = ov;
+  if (bf16_k) {
+    // 32-bit buffer offsets: a chunk's bytes must stay below 2^31 (also
+    // under the override)
+    const long long need = ((long long)B * T_max * d * 2 >> 30) + 1;
+    if (nch < need) nch = need;
+  }
   if (nch > (1 << 20)) return false;
   p->nch = (int)nch;
   p->nslots = p->nch + B - 1;
@@ -87,7 +93,10 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
     p->proj_rows = grid * 2 >= ncu ? big : proj_rows(dh, false);
   }
   p->npc = (d + p->proj_rows - 1) / p->proj_rows;
-  size_t off = 0;
+  // control block first: status word, arrival counter
+  p->off_status = 0;
+  p->off_tickets = 8;
+  size_t off = 256;
   p->off_U = off;
   off += align256((size_t)p->nslots * H * d * sizeof(float));
   p->off_ml = off;
@@ -97,8 +106,6 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   p->xchg = bf16_k && p->gc == 2 && dh == 128 && 2 * p->dc == d && p->nw == 8;
   p->off_mbox = off;
   off += p->xchg ? align256((size_t)p->nch * 2 * 8 * 8 * 16 * sizeof(unsigned long long)) : 0;
-  p->off_tickets = off;
-  off += 256;
   p->bytes = off;
   return true;
 }
@@ -120,6 +127,7 @@ const char* slim_status_string(slim_status_t s) {
     case SLIM_ERR_WORKSPACE: return "workspace too small";
     case SLIM_ERR_HIP: return "HIP runtime error";
     case SLIM_ERR_SINGULAR: return "W_K is singular";
+    case SLIM_ERR_TIMEOUT: return "an attend workgroup gave up waiting for its partner";
   }
   return "unknown status";
 }
@@ -218,6 +226,7 @@ static slim_status_t decode_prepare(const float* q, const void* K_cache, slim_dt
   a->scale = scale;
   a->w_bf16 = w_dt == SLIM_BF16;
   a->ws = static_cast<char*>(workspace);
+  a->status = reinterpret_cast<uint32_t*>(a->ws + plan->off_status);
   return SLIM_OK;
 }
 
@@ -264,6 +273,15 @@ slim_status_t slim_decode_finish(const float* q, const void* K_cache, slim_dtype
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(kFinish, q, K_cache, k_dt, lengths, W_KV, w_dt, out, B, H, dh, T_max, scale,
                        workspace, workspace_bytes, stream);
+}
+
+slim_status_t slim_decode_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes < 256 || !aligned16(workspace)) return SLIM_ERR_INVALID;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return SLIM_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SLIM_ERR_HIP;
+  return word == 0 ? SLIM_OK : SLIM_ERR_TIMEOUT;
 }
 
 size_t slim_step_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t k_dt) {

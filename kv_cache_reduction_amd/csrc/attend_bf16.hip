@@ -59,6 +59,7 @@ struct AttendBf16Params {
   const int32_t* lengths;
   float* U;
   float* ml;
+  uint32_t* status;  // cleared here; the finish sets it if a piece is marked failed
   int B, H, d, T_max, nch, dc, nslots;
   float qscale;
 };
@@ -190,6 +191,7 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  if (blockIdx.x == 0 && tid == 0) *p.status = 0u;
 
   int c, cg;
   {
@@ -449,12 +451,15 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
 constexpr int kXchgLook = 3;
 constexpr int kMboxDepth = 8;                  // mailbox ring depth in steps
 constexpr uint32_t kPollSpinLimit = 1u << 19;  // re-polls (about a second) before giving up
+constexpr uint32_t kEpochMask = 0x7fffffu;     // 23 bits: a tag never has its top bit set
 
 struct XchgParams {
   AttendBf16Params a;
   unsigned long long* mbox;     // [nch][2][kMboxDepth][8 waves][16] {tag, score}
   unsigned long long* tickets;  // arrival counter (any initial value)
-  uint32_t epoch;            // 24 bits used
+  uint32_t epoch;               // kEpochMask bits used
+  uint32_t spin_limit;          // re-polls of one wait before the piece is marked failed
+  uint32_t pub_skew;            // testing: added to the epoch of column group 1's entries
 };
 
 __device__ __forceinline__ void dma16_sc1(uint32_t lds, const i32x4& rsrc, uint32_t voff) {
@@ -491,6 +496,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  if (blockIdx.x == 0 && tid == 0) *p.status = 0u;
   // Roles by arrival: role = (ticket mod grid size); roles 2c and 2c+1 form
   // chunk c's pair.  Any gridDim.x consecutive tickets cover every role
   // once, whatever the counter held before, and a workgroup's partner is
@@ -530,7 +536,8 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
   const uint32_t qbuf_s = (uint32_t)reinterpret_cast<uintptr_t>(qbuf + wave * kMfmaUnitCols);
   const int r16 = lane & 15;
   const int pub_e = (l32 >> 4) * 8 + half * 4 + 2 * (r16 & 1) + (r16 >> 1);  // valid for r16 < 4
-  const uint32_t ep = (xp.epoch & 0xffffffu) << 8;
+  const uint32_t ep = (xp.epoch & kEpochMask) << 8;
+  const uint32_t ep_pub = ((xp.epoch + (cg ? xp.pub_skew : 0u)) & kEpochMask) << 8;
   bool failed = false;
 
   int gstep = 0;  // step counter across pieces (tags, score buffers)
@@ -568,7 +575,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
       if (r16 < 4) {
         S[(gs & (NS - 1)) * 256 + (ocol / DH) * 8 + (pub_e & 7)] = x;
         const unsigned long long ent =
-            ((unsigned long long)(ep | (((uint32_t)gs / kMboxDepth) & 0xffu)) << 32) | __float_as_uint(x);
+            ((unsigned long long)(ep_pub | (((uint32_t)gs / kMboxDepth) & 0xffu)) << 32) | __float_as_uint(x);
         __hip_atomic_store(mine + (size_t)((uint32_t)gs % kMboxDepth) * 8 * 16 + pub_e, ent, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -596,7 +603,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
       const int gs = gstep + step;
       uint32_t tries = 0;
       while (!try_check(step)) {
-        if (failed || ++tries > kPollSpinLimit) {
+        if (failed || ++tries > xp.spin_limit) {
           failed = true;
           if (lane < 16) S[(gs & (NS - 1)) * 256 + (xbase / DH + (lane >> 3)) * 8 + (lane & 7)] = __uint_as_float(kQuietNaN);
           break;
@@ -741,6 +748,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   p.lengths = a.lengths;
   p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
   p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
+  p.status = a.status;
   p.B = a.B;
   p.H = a.H;
   p.d = a.d;
@@ -758,7 +766,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   return hipGetLastError();
 }
 
-// Per-launch epoch of the mailbox tags (24 bits used): distinct for 2^24
+// Per-launch epoch of the mailbox tags (23 bits used): distinct for 2^23
 // consecutive launches of the process, and started at a random value so
 // that another process's entries left in reused device memory do not match.
 static uint32_t epoch_seed() {
@@ -770,12 +778,26 @@ static uint32_t next_epoch() {
   return ctr.fetch_add(1) + 1;
 }
 
+// Sets every mailbox entry to all ones: a tag no launch writes (tags keep
+// their top bit clear).
+__global__ void __launch_bounds__(256) mbox_reset_kernel(unsigned long long* __restrict__ mbox, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) mbox[i] = ~0ull;
+}
+
 // Launches the exchange kernel when the shape allows it (two full column
 // groups of dh = 128); returns hipErrorNotSupported otherwise, and the caller
 // falls back.
+//
+// The epoch is a kernel argument.  A launch recorded into a graph replays
+// with the same epoch, so entries left by the previous replay would carry
+// the expected tags; while the stream is capturing, a reset of the mailbox
+// is recorded in front of the attend, and every replay starts from entries
+// no tag matches.
 static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
   constexpr int NST = 4;
   if (!pl.xchg || env_int("SLIM_XCHG", 1) == 0) return hipErrorNotSupported;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return hipErrorInvalidValue;
   XchgParams xp;
   AttendBf16Params& p = xp.a;
   p.q = a.q;
@@ -783,6 +805,7 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   p.lengths = a.lengths;
   p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
   p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
+  p.status = a.status;
   p.B = a.B;
   p.H = a.H;
   p.d = a.d;
@@ -794,6 +817,18 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   xp.mbox = reinterpret_cast<unsigned long long*>(a.ws + pl.off_mbox);
   xp.tickets = reinterpret_cast<unsigned long long*>(a.ws + pl.off_tickets);
   xp.epoch = next_epoch();
+  // testing knobs: the wait bound, and a skew that keeps one column group's
+  // entries from ever matching (every wait then runs out of its bound)
+  const int spin = env_int("SLIM_XCHG_SPIN", -1);
+  xp.spin_limit = spin >= 0 ? (uint32_t)spin : kPollSpinLimit;
+  xp.pub_skew = (uint32_t)env_int("SLIM_XCHG_SKEW", 0);
+  if (cap == hipStreamCaptureStatusActive) {
+    const size_t n = (size_t)pl.nch * 2 * kMboxDepth * 8 * 16;
+    const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(mbox_reset_kernel, dim3(blocks), dim3(256), 0, s, xp.mbox, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const size_t lds = (size_t)pl.nw * NST * 4 * (1024 + 64) + 4 * 256 * sizeof(float) +
                      (size_t)pl.nw * 32 * sizeof(unsigned long long) + (size_t)pl.nw * kMfmaUnitCols * sizeof(float) +
                      (16 + (size_t)a.B + 1) * sizeof(int);

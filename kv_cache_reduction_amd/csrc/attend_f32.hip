@@ -9,8 +9,11 @@
 //   U[h, col] = alpha_h * U[h, col] + p_h * K[t, col].
 // Every workgroup recomputes the scores of all heads (each needs all d
 // columns of the row); this path serves small fp32 problems.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
+#include "launch.hpp"
 
 namespace slim {
 
@@ -20,6 +23,7 @@ struct AttendF32Params {
   const int32_t* lengths;
   float* U;
   float* ml;
+  uint32_t* status;  // cleared here; the finish sets it if a piece is marked failed
   int B, H, dh, d, T_max, nch, gcf, nslots;
   float qscale;
 };
@@ -34,6 +38,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
   int* pre = reinterpret_cast<int*>(row + p.d);           // [B + 1]
 
   const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) *p.status = 0u;
   const int c = blockIdx.x / p.gcf, cb = blockIdx.x % p.gcf;
   const int col = cb * 256 + tid;
   const bool col_ok = col < p.d;
@@ -102,6 +107,7 @@ hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStrea
   p.lengths = a.lengths;
   p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
   p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
+  p.status = a.status;
   p.B = a.B;
   p.H = a.H;
   p.dh = a.dh;
@@ -112,6 +118,9 @@ hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStrea
   p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
   const size_t lds = (4 + 2 * kF32MaxHeads + (size_t)a.d + (size_t)a.B + 1) * 4;
+  static std::atomic<int> granted[kMaxDevices];
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(attend_f32_kernel), lds, granted);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_f32_kernel, dim3(pl.nch * pl.gc), dim3(256), lds, s, p);
   return hipGetLastError();
 }

@@ -56,7 +56,8 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
                                                             const float* __restrict__ U,
                                                             const float* __restrict__ ml,
                                                             const void* __restrict__ W,
-                                                            float* __restrict__ part, int B, int H, int d,
+                                                            float* __restrict__ part,
+                                                            uint32_t* __restrict__ status, int B, int H, int d,
                                                             int T_max, int nch, int nslots, int fixed_ns,
                                                             int spw) {
   // projection: thread t covers JW output columns (group jq = t % JQ) over the
@@ -215,6 +216,7 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
       mstar[2 * slot_id] = m;
       mstar[2 * slot_id + 1] = bad ? __builtin_nanf("") : l;
     }
+    if (bad && status) *status = 1u;  // an attend piece gave up: report it
     __syncthreads();
     for (int r = tid; r < G * PR; r += 256) {
       const int gg = r / PR, rw = r % PR;
@@ -353,10 +355,10 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   const dim3 grid(a.H, pl.npc, (a.B + spw - 1) / spw);
   if (mp)
     hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, MFMA_OK>), grid, dim3(256), lds, s, a.lengths, U, ml,
-                       a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+                       a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   else
     hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false>), grid, dim3(256), lds, s, a.lengths, U, ml,
-                       a.W, part, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+                       a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;

@@ -26,6 +26,7 @@ struct DecodePlan {
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
   bool xchg;       // two equal column groups whose workgroups exchange scores
   size_t off_mbox; // [nch, 2, 8, 8, 16] u64 score mailboxes of the exchange
+  size_t off_status;   // u32 status word (0 = ok); cleared by the attend, set by the finish
   size_t off_tickets;  // u64 arrival counter of the exchange workgroups
   size_t bytes;
 };
@@ -40,6 +41,7 @@ struct DecodeArgs {
   float scale;
   bool w_bf16;
   char* ws;
+  uint32_t* status;  // workspace status word (decode and step), or null
 };
 
 // W_KV rows per finish workgroup: a multiple of the projection's row subsets
