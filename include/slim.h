@@ -158,6 +158,29 @@ slim_status_t slim_decode(const float* q,
                           hipStream_t stream);
 
 /*
+ * slim_decode_noalloc -- slim_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments and results without a workspace.
+ * Its workspace is a device array inside the library, SLIM_NOALLOC_SCRATCH_BYTES
+ * bytes per device, reserved when the library's code is loaded on a device
+ * and held until the process ends; the call itself allocates nothing.
+ * Shapes whose slim_decode_workspace_bytes exceeds that size are rejected
+ * with SLIM_ERR_WORKSPACE (nothing is enqueued).  Every call on one device
+ * shares that device's array: calls that may overlap on one device (other
+ * streams, other threads) race and must not be issued; consecutive calls on
+ * one stream are fine.  slim_decode_status cannot be queried for these
+ * calls (the array is not the caller's).
+ */
+#define SLIM_NOALLOC_SCRATCH_BYTES (80u << 20)
+slim_status_t slim_decode_noalloc(const float* q,
+                                  const void* K_cache, slim_dtype_t k_dt,
+                                  const int32_t* lengths,
+                                  const void* W_KV, slim_dtype_t w_dt,
+                                  float* out,
+                                  int B, int H, int dh, int T_max, float scale,
+                                  hipStream_t stream);
+
+/*
  * slim_decode_status -- the device-side outcome of the last slim_decode,
  * slim_step or attend + finish pair that used `workspace` (the first 256
  * bytes of a decode or step workspace hold a status word: the attend clears

@@ -43,6 +43,9 @@ for _name in ("slim_decode", "slim_decode_attend", "slim_decode_finish"):
     _fn = getattr(lib, _name)
     _fn.restype = _i
     _fn.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp, _sz, _vp]
+lib.slim_decode_noalloc.restype = _i
+lib.slim_decode_noalloc.argtypes = [_vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _f, _vp]
+NOALLOC_SCRATCH_BYTES = 80 << 20
 lib.slim_decode_status.restype = _i
 lib.slim_decode_status.argtypes = [_vp, _sz, _vp]
 lib.slim_step_workspace_bytes.restype = _sz
@@ -156,6 +159,10 @@ def workspace(nbytes: int, device="cuda"):
 
 
 def _decode_args(q, K_cache, lengths, W_KV, out, H, dh, scale, ws):
+    return _decode_core(q, K_cache, lengths, W_KV, out, H, dh, scale) + (_dev(ws), ws.numel())
+
+
+def _decode_core(q, K_cache, lengths, W_KV, out, H, dh, scale):
     B, T_max, d = K_cache.shape
     if d != H * dh or q.shape != (B, d) or out.shape != (B, H, dh) or lengths.shape != (B,):
         raise ValueError("shape mismatch")
@@ -166,7 +173,7 @@ def _decode_args(q, K_cache, lengths, W_KV, out, H, dh, scale, ws):
         raise TypeError("q and out are float32, lengths int32")
     scale = 1.0 / math.sqrt(dh) if scale is None else float(scale)
     return (_dev(q), _dev(K_cache), _dt(K_cache), _dev(lengths), _dev(W_KV), _dt(W_KV), _dev(out),
-            B, H, dh, T_max, scale, _dev(ws), ws.numel())
+            B, H, dh, T_max, scale)
 
 
 def decode(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, stream=None) -> None:
@@ -176,6 +183,13 @@ def decode(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, stream=No
                        q.device)
     _check(lib.slim_decode(*_decode_args(q, K_cache, lengths, W_KV, out, H, dh, scale, ws),
                            _stream(stream)), "slim_decode")
+
+
+def decode_noalloc(q, K_cache, lengths, W_KV, out, H, dh, scale=None, stream=None) -> None:
+    """slim_decode without a workspace (see slim_decode_noalloc in
+    include/slim.h): the library's own device array serves as scratch."""
+    _check(lib.slim_decode_noalloc(*_decode_core(q, K_cache, lengths, W_KV, out, H, dh, scale),
+                                   _stream(stream)), "slim_decode_noalloc")
 
 
 def decode_attend(q, K_cache, lengths, W_KV, out, H, dh, scale=None, ws=None, stream=None) -> None:

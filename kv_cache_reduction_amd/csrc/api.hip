@@ -114,6 +114,27 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
 
 using namespace slim;
 
+// Workspace of slim_decode_noalloc: a file-scope device array, one copy per
+// device, held until the process ends.  In host code `scratch` only names
+// the symbol; its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SLIM_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null on failure.
+static void* scratch_ptr() {
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  cache[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -257,6 +278,25 @@ slim_status_t slim_decode(const float* q, const void* K_cache, slim_dtype_t k_dt
                           size_t workspace_bytes, hipStream_t stream) {
   return decode_common(kFull, q, K_cache, k_dt, lengths, W_KV, w_dt, out, B, H, dh, T_max, scale,
                        workspace, workspace_bytes, stream);
+}
+
+slim_status_t slim_decode_noalloc(const float* q, const void* K_cache, slim_dtype_t k_dt,
+                                  const int32_t* lengths, const void* W_KV, slim_dtype_t w_dt, float* out,
+                                  int B, int H, int dh, int T_max, float scale, hipStream_t stream) {
+  DecodePlan plan;
+  DecodeArgs a;
+  // the argument checks need a non-null, aligned workspace pointer: the
+  // scratch address is looked up only once they pass
+  static const char kProbe alignas(256) = 0;
+  slim_status_t st = decode_prepare(q, K_cache, k_dt, lengths, W_KV, w_dt, out, B, H, dh, T_max, scale,
+                                    const_cast<char*>(&kProbe), &plan, &a);
+  if (st != SLIM_OK) return st;
+  if (plan.bytes > (size_t)SLIM_NOALLOC_SCRATCH_BYTES) return SLIM_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return SLIM_ERR_HIP;
+  a.ws = static_cast<char*>(ws);
+  a.status = reinterpret_cast<uint32_t*>(a.ws + plan.off_status);
+  return decode_launch(kFull, plan, a, stream) == hipSuccess ? SLIM_OK : SLIM_ERR_HIP;
 }
 
 slim_status_t slim_decode_attend(const float* q, const void* K_cache, slim_dtype_t k_dt,
