@@ -5,11 +5,22 @@ softmax-times-K over the whole K cache; finish: chunk merge and W_KV
 projection) for one new token per sequence.  W_KV (host, once per layer) and
 the K cache write (prefill) happen before the timed region.
 
-Default workload: long-context single-stream decode, d=4096, H=32, dh=128,
-B=1, T=131072, bf16 K cache and W_KV.  Inputs are synthetic and seeded; the
-K cache is written on the device by slim_prefill from bf16 X and W_K, and two
-copies are rotated so the 256 MB Infinity Cache cannot serve a step from the
-previous one.
+Headline workload: long-context single-stream decode, d=4096, H=32, dh=128,
+B=1, T=131072, bf16 K cache and W_KV.  Every other decode workload is timed
+the same way and reported under "shapes" (tiny fp32, GPT-2-small-shaped,
+7B-shaped ragged and at uniform T=8192, Whisper-large-shaped).  Inputs are
+synthetic and seeded; K caches are written on the device by slim_prefill,
+and copies totalling at least 512 MiB are rotated so that the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Timing per workload (HIP events on the stream the library launches on):
+  * `steps` decode calls back to back between two events: the step time
+    (`value`, `ms_per_step`);
+  * max(steps, 50) calls, each between its own event pair: the median, p10
+    and p90 of the step (each interval includes one event record);
+  * max(steps, 50) calls with event pairs around the attend and the finish
+    launches separately: their distributions (the attend's mean is the
+    roofline's kernel time).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -30,8 +41,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode tokens/s and K-cache GB/s (% HBM peak) at T=8K/128K, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
+ROTATE_MIN_BYTES = 512 << 20
+DIST_STEPS = 50
 ATTEND_SOURCES = ["kv_cache_reduction_amd/csrc/attend_bf16.hip", "kv_cache_reduction_amd/csrc/common.hpp",
                   "kv_cache_reduction_amd/csrc/internal.hpp"]
+SHAPES = ["tiny_f32", "gpt2_small", "7b_ragged", "7b_8k", "whisper_large"]
 
 
 def log(*a):
@@ -43,97 +57,192 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="long_128k", choices=["gpt2_small", "7b_ragged", "7b_8k", "long_128k", "whisper_large"])
+    ap.add_argument("--config", default="long_128k", choices=["long_128k"] + SHAPES)
+    ap.add_argument("--shapes", default="all", help="comma list of other workloads to time, 'all' or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip comparator, T=8K point, probe")
+    ap.add_argument("--no-extras", action="store_true", help="skip generation step, many queries, comparators, probes")
     return ap.parse_args()
 
 
 # ---------------------------------------------------------------------------
-# device workload
+# device workloads
 
-def bf16_dev(bits: np.ndarray):
-    import torch
+def dev_bits(torch, bits: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def build_cache(cfg, w, W, lens, torch, slim):
-    """Cache rows round(X_b . W) for every sequence, written on the device by
-    slim_prefill from bf16 X (seeded rows) and bf16 W."""
+def dev_store(torch, cfg, x32: np.ndarray):
+    """float32 host array -> device tensor in the cache storage format."""
     import synthetic as syn
-    K = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=torch.bfloat16, device="cuda")
-    Wd = bf16_dev(syn.f32_to_bf16_bits(W.astype(np.float32)))
+    if cfg.cache == "bf16":
+        return dev_bits(torch, syn.f32_to_bf16_bits(np.asarray(x32, dtype=np.float32)))
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).cuda()
+
+
+def build_cache(cfg, W, lens, torch, slim):
+    """Cache rows round(X_b . W) for every sequence, written on the device by
+    slim_prefill from X (seeded rows) and W in the cache storage format."""
+    import synthetic as syn
+    dt = torch.bfloat16 if cfg.cache == "bf16" else torch.float32
+    K = torch.zeros((cfg.B, cfg.T_max, cfg.d), dtype=dt, device="cuda")
+    Wd = dev_store(torch, cfg, W.astype(np.float32))
     blk = 8192
     for b in range(cfg.B):
         n = int(lens[b])
         for t0 in range(0, n, blk):
             t1 = min(n, t0 + blk)
-            X = bf16_dev(syn.f32_to_bf16_bits(syn.x_rows(cfg, b, t0, t1)))[None]
+            X = dev_store(torch, cfg, syn.x_rows(cfg, b, t0, t1))[None]
             t0d = torch.tensor([t0], dtype=torch.int32, device="cuda")
             slim.prefill(X, Wd, K[b:b + 1], t0=t0d)
     torch.cuda.synchronize()
     return K
 
 
+def rotation_copies(cache_bytes: int) -> int:
+    """Copies of a cache whose rotation spans at least 512 MiB (and two), at
+    most 1024: a cache of a few KB is launch-bound, not cache-bound."""
+    return min(1024, max(2, -(-ROTATE_MIN_BYTES // cache_bytes) + 1))
+
+
+_WEIGHTS = {}
+
+
 class Workload:
-    def __init__(self, name, torch, slim, with_v=False, rotate=2):
+    def __init__(self, name, torch, slim, with_v=False):
         import synthetic as syn
+        self.name = name
         self.cfg = cfg = syn.CONFIGS[name]
         t = time.time()
-        w = syn.weights(cfg)
-        # the device K cache is built from bf16 W_K, so W_KV comes from the same matrix
-        WK = syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))).astype(np.float64)
+        key = (cfg.seed, cfg.d, cfg.weights_bf16)
+        if key not in _WEIGHTS:
+            w = syn.weights(cfg)
+            # the device K cache is built from W_K in the cache format, so W_KV comes from that matrix
+            WK = (syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))) if cfg.cache == "bf16"
+                  else w.W_K.astype(np.float32)).astype(np.float64)
+            Wkv = slim.wkv(WK, w.W_V, cfg.wkv)
+            _WEIGHTS.clear()
+            _WEIGHTS[key] = (w, WK, Wkv)
+        w, WK, Wkv = _WEIGHTS[key]
         self.lens = syn.lengths(cfg)
         self.w, self.WK = w, WK
         self.q = torch.from_numpy(syn.queries(cfg, w)).cuda()
         self.ld = torch.from_numpy(self.lens).cuda()
-        log(f"[bench] {name}: weights {time.time() - t:.1f}s")
+        self.W = dev_bits(torch, Wkv) if cfg.wkv == "bf16" else torch.from_numpy(Wkv).cuda()
+        log(f"[bench] {name}: weights and W_KV {time.time() - t:.1f}s")
         t = time.time()
-        W = slim.wkv(WK, w.W_V, cfg.wkv)
-        self.W = bf16_dev(W) if cfg.wkv == "bf16" else torch.from_numpy(W).cuda()
-        log(f"[bench] {name}: W_KV (host LU, d={cfg.d}) {time.time() - t:.1f}s")
-        t = time.time()
-        K0 = build_cache(cfg, w, WK, self.lens, torch, slim)
-        self.K = [K0] + [K0.clone() for _ in range(rotate - 1)]
+        K0 = build_cache(cfg, WK, self.lens, torch, slim)
+        alloc = K0.numel() * K0.element_size()
+        self.K = [K0] + [K0.clone() for _ in range(rotation_copies(alloc) - 1)]
         self.V = None
-        if with_v:
-            V0 = build_cache(cfg, w, w.W_V, self.lens, torch, slim)
-            self.V = [V0] + [V0.clone() for _ in range(rotate - 1)]
-        log(f"[bench] {name}: caches via prefill {time.time() - t:.1f}s")
+        if with_v and cfg.cache == "bf16":
+            V0 = build_cache(cfg, w.W_V, self.lens, torch, slim)
+            self.V = [V0] + [V0.clone() for _ in range(rotation_copies(alloc) - 1)]
+        log(f"[bench] {name}: {len(self.K)} rotated K copies ({len(self.K) * alloc / 2**20:.0f} MiB)"
+            f"{' and V copies' if self.V else ''} via prefill {time.time() - t:.1f}s")
         self.out = torch.empty((cfg.B, cfg.H, cfg.dh), dtype=torch.float32, device="cuda")
-        self.ws = slim.workspace(slim.decode_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, slim.BF16))
-        self.kv_ws = slim.workspace(slim.mha_kv_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, slim.BF16))
-        self.k_bytes = int(self.lens.astype(np.int64).sum()) * cfg.d * 2
+        self.ws = slim.workspace(slim.decode_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, K0.dtype))
+        self.kv_ws = (slim.workspace(slim.mha_kv_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, K0.dtype))
+                      if self.V else None)
+        self.k_bytes = int(self.lens.astype(np.int64).sum()) * cfg.d * K0.element_size()
+
+    def args(self, i):
+        cfg = self.cfg
+        return (self.q, self.K[i % len(self.K)], self.ld, self.W, self.out, cfg.H, cfg.dh, cfg.scale, self.ws)
 
 
-def time_slim(wl, torch, slim, steps, warmup):
-    """Step time: `steps` slim_decode calls back to back between two events.
-    Attend time (for the roofline): a second loop with an event pair around
-    each attend launch; those events sit between kernels, so this loop is
-    not used for the step time."""
-    cfg = wl.cfg
-    args = lambda i: (wl.q, wl.K[i % len(wl.K)], wl.ld, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, wl.ws)
-    for i in range(warmup):
-        slim.decode(*args(i))
-    torch.cuda.synchronize()
+def _stats(us: np.ndarray) -> dict:
+    return {"mean": float(us.mean()), "median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "n": int(us.size)}
+
+
+def _loop_ms(torch, fn, steps):
     E = torch.cuda.Event
     start, stop = E(enable_timing=True), E(enable_timing=True)
     start.record()
     for i in range(steps):
-        slim.decode(*args(i))
+        fn(i)
     stop.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / steps
-    a0 = [E(enable_timing=True) for _ in range(steps)]
-    a1 = [E(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        a0[i].record()
-        slim.decode_attend(*args(i))
-        a1[i].record()
-        slim.decode_finish(*args(i))
+    return start.elapsed_time(stop) / steps
+
+
+def time_decode(wl, torch, slim, steps, warmup):
+    """Step time from `steps` back-to-back slim_decode calls; per-step and
+    per-phase distributions from event-bracketed calls."""
+    for i in range(warmup):
+        slim.decode(*wl.args(i))
     torch.cuda.synchronize()
-    attend = np.array([a0[i].elapsed_time(a1[i]) for i in range(steps)])
-    return ms_step, attend
+    ms_step = _loop_ms(torch, lambda i: slim.decode(*wl.args(i)), steps)
+    n = max(steps, DIST_STEPS)
+    E = torch.cuda.Event
+    e = [[E(enable_timing=True) for _ in range(n)] for _ in range(3)]
+    for i in range(n):
+        e[0][i].record()
+        slim.decode(*wl.args(i))
+        e[1][i].record()
+    torch.cuda.synchronize()
+    step_us = np.array([e[0][i].elapsed_time(e[1][i]) for i in range(n)]) * 1e3
+    for i in range(n):
+        e[0][i].record()
+        slim.decode_attend(*wl.args(i))
+        e[1][i].record()
+        slim.decode_finish(*wl.args(i))
+        e[2][i].record()
+    torch.cuda.synchronize()
+    attend_us = np.array([e[0][i].elapsed_time(e[1][i]) for i in range(n)]) * 1e3
+    finish_us = np.array([e[1][i].elapsed_time(e[2][i]) for i in range(n)]) * 1e3
+    st = slim.decode_status(wl.ws)
+    if st != 0:
+        raise RuntimeError(f"{wl.name}: decode reported status {st}")
+    return ms_step, _stats(step_us), _stats(attend_us), _stats(finish_us)
+
+
+def time_kv(wl, torch, slim, steps, warmup):
+    cfg = wl.cfg
+    fn = lambda i: slim.mha_decode_kv(wl.q, wl.K[i % len(wl.K)], wl.V[i % len(wl.V)], wl.ld, wl.out, cfg.H,
+                                      cfg.dh, cfg.scale, wl.kv_ws)
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    return _loop_ms(torch, fn, steps)
+
+
+def attend_kernel_name(cfg):
+    """The attend kernel the library picks for this shape: the score
+    exchange between the two column groups for d = 2*dc with dh = 128 (d a
+    multiple of 512 above 2048), the one-workgroup-per-column-group kernel
+    for other bf16 caches, the fp32 kernel for fp32 caches."""
+    if cfg.cache != "bf16":
+        return "slim::attend_f32_kernel"
+    xchg = (cfg.dh == 128 and cfg.d > 2048 and cfg.d % 512 == 0
+            and os.environ.get("SLIM_XCHG", "1") != "0")
+    return "slim::attend_xchg_kernel<4>" if xchg else "slim::attend_bf16_kernel"
+
+
+def decode_record(wl, torch, slim, steps, warmup, with_kv):
+    cfg = wl.cfg
+    log(f"[bench] timing {wl.name}: {warmup} warmup + {steps} steps (+ {max(steps, DIST_STEPS)} bracketed)")
+    ms_step, step, attend, finish = time_decode(wl, torch, slim, steps, warmup)
+    gbps = wl.k_bytes / (ms_step * 1e-3) / 1e9
+    att_gbps = wl.k_bytes / (attend["mean"] * 1e-6) / 1e9
+    rec = {"workload": cfg.desc, "B": cfg.B, "d": cfg.d, "H": cfg.H, "dh": cfg.dh, "T_max": cfg.T_max,
+           "k_bytes": wl.k_bytes, "rotated_copies": len(wl.K),
+           "tokens_s": cfg.B / (ms_step * 1e-3), "ms_per_step": ms_step,
+           "k_cache_gbps": gbps, "k_cache_hbm_frac": gbps / HBM_PEAK_GBPS,
+           "attend_gbps": att_gbps, "attend_hbm_frac": att_gbps / HBM_PEAK_GBPS,
+           "attend_kernel": attend_kernel_name(cfg),
+           "step_us": step, "attend_us": attend, "finish_us": finish,
+           "finish_share_of_step": finish["mean"] / (ms_step * 1e3)}
+    log(f"[bench] {wl.name}: {ms_step * 1e3:.1f} us/step (median {step['median']:.1f}, p10 {step['p10']:.1f}, "
+        f"p90 {step['p90']:.1f}), attend {attend['mean']:.1f} us ({att_gbps:.0f} GB/s), finish "
+        f"{finish['mean']:.1f} us, {rec['tokens_s']:.1f} tokens/s, step K-rate {gbps:.0f} GB/s")
+    if with_kv and wl.V is not None:
+        ms_kv = time_kv(wl, torch, slim, steps, 3)
+        rec["comparator"] = {"what": "standard MHA decode over explicit bf16 K and V caches (same box)",
+                             "tokens_s": cfg.B / (ms_kv * 1e-3), "ms_per_step": ms_kv,
+                             "kv_gbps": 2 * wl.k_bytes / (ms_kv * 1e-3) / 1e9, "slim_speedup": ms_kv / ms_step}
+        log(f"[bench] {wl.name}: comparator {ms_kv * 1e3:.1f} us/step, slim speedup {ms_kv / ms_step:.2f}x")
+    return rec
 
 
 def time_step(wl, torch, slim, steps, warmup):
@@ -142,38 +251,17 @@ def time_step(wl, torch, slim, steps, warmup):
     row len_b - 1 (the same row every step, so the cache never fills)."""
     import synthetic as syn
     cfg = wl.cfg
-    WQ = bf16_dev(syn.f32_to_bf16_bits(wl.w.W_Q.astype(np.float32)))
-    WK = bf16_dev(syn.f32_to_bf16_bits(wl.WK.astype(np.float32)))
+    WQ = dev_bits(torch, syn.f32_to_bf16_bits(wl.w.W_Q.astype(np.float32)))
+    WK = dev_bits(torch, syn.f32_to_bf16_bits(wl.WK.astype(np.float32)))
     x = torch.from_numpy(syn.x_new(cfg)).cuda()
     lens = torch.from_numpy(np.maximum(wl.lens - 1, 0).astype(np.int32)).cuda()
     nxt = torch.empty_like(lens)
     ws = slim.workspace(slim.step_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, slim.BF16))
-    args = lambda i: (x, WQ, WK, wl.K[i % len(wl.K)], lens, nxt, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, ws)
+    fn = lambda i: slim.step(x, WQ, WK, wl.K[i % len(wl.K)], lens, nxt, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, ws)
     for i in range(warmup):
-        slim.step(*args(i))
+        fn(i)
     torch.cuda.synchronize()
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        slim.step(*args(i))
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
-
-
-def _event_ms(torch, fn, steps, warmup):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        fn()
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    return _loop_ms(torch, fn, steps)
 
 
 def _graph_ms(torch, fn, out, steps):
@@ -198,14 +286,9 @@ def _graph_ms(torch, fn, out, steps):
         torch.cuda.synchronize()
         if not torch.equal(out, ref):
             raise RuntimeError("graph replay differs from the eager call")
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    start.record()
-    for _ in range(steps):
-        g.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    ms = _loop_ms(torch, lambda i: g.replay(), steps)
+    del g
+    return ms
 
 
 def multi_query_flops(n, H, dh, T, limits, option):
@@ -235,9 +318,9 @@ def time_multi(torch, slim, steps):
         one = syn.shrink(cfg, B=1)
         Xb = syn.f32_to_bf16_bits(syn.x_rows(one, 0, 0, T))
         K = torch.zeros((1, T, cfg.d), dtype=torch.bfloat16, device="cuda")
-        slim.prefill(bf16_dev(Xb)[None], bf16_dev(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))), K)
+        slim.prefill(dev_bits(torch, Xb)[None], dev_bits(torch, syn.f32_to_bf16_bits(w.W_K.astype(np.float32))), K)
         K = K[0]
-        Wkv = bf16_dev(slim.wkv(syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))).astype(
+        Wkv = dev_bits(torch, slim.wkv(syn.bf16_bits_to_f32(syn.f32_to_bf16_bits(w.W_K.astype(np.float32))).astype(
             np.float64), w.W_V, "bf16"))
         if causal:
             X = syn.x_rows(one, 0, T - n, T).astype(np.float64)
@@ -263,38 +346,23 @@ def time_multi(torch, slim, steps):
     return out
 
 
-def time_kv(wl, torch, slim, steps, warmup):
-    cfg = wl.cfg
-    args = lambda i: (wl.q, wl.K[i % len(wl.K)], wl.V[i % len(wl.V)], wl.ld, wl.out, cfg.H, cfg.dh,
-                      cfg.scale, wl.kv_ws)
-    for i in range(warmup):
-        slim.mha_decode_kv(*args(i))
-    torch.cuda.synchronize()
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        slim.mha_decode_kv(*args(i))
-    stop.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
-
-
 def probe_copy_gbps(torch, slim, dst, src):
     """Plain copy of a known size (read + write); its counter readings
     calibrate FETCH_SIZE / WRITE_SIZE."""
     for _ in range(2):
         slim.probe_copy(dst, src)
     torch.cuda.synchronize()
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    n = 5
-    start.record()
-    for _ in range(n):
-        slim.probe_copy(dst, src)
-    stop.record()
+    ms = _loop_ms(torch, lambda i: slim.probe_copy(dst, src), 5)
+    return 2 * src.numel() * src.element_size() / (ms * 1e-3) / 1e9
+
+
+def probe_read_gbps(torch, slim, src):
+    sink = torch.empty(slim.probe_sink_floats(), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        slim.probe_read(src, sink)
     torch.cuda.synchronize()
-    return 2 * src.numel() * src.element_size() / (start.elapsed_time(stop) / n * 1e-3) / 1e9
+    ms = _loop_ms(torch, lambda i: slim.probe_read(src, sink), 10)
+    return src.numel() * src.element_size() / (ms * 1e-3) / 1e9
 
 
 def measured_traffic(kernel_sources):
@@ -313,78 +381,57 @@ def measured_traffic(kernel_sources):
     return rec.get("hbm_bytes_per_launch")
 
 
-def attend_kernel_name(cfg):
-    """The attend kernel the library picks for this shape: the score
-    exchange between the two column groups for d = 2*dc with dh = 128 (d a
-    multiple of 512 above 2048), the one-workgroup-per-column-group kernel
-    otherwise."""
-    xchg = (cfg.dh == 128 and cfg.d > 2048 and cfg.d % 512 == 0
-            and os.environ.get("SLIM_XCHG", "1") != "0")
-    return "slim::attend_xchg_kernel<4>" if xchg else "slim::attend_bf16_kernel"
-
-
-def probe_read_gbps(torch, slim, src):
-    sink = torch.empty(slim.probe_sink_floats(), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        slim.probe_read(src, sink)
-    torch.cuda.synchronize()
-    E = torch.cuda.Event
-    start, stop = E(enable_timing=True), E(enable_timing=True)
-    n = 10
-    start.record()
-    for _ in range(n):
-        slim.probe_read(src, sink)
-    stop.record()
-    torch.cuda.synchronize()
-    return src.numel() * src.element_size() / (start.elapsed_time(stop) / n * 1e-3) / 1e9
-
-
 # ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample of the same workload
 
-def cpu_baseline(name, T_sample=16384, min_seconds=10.0):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or ""
+
+
+def cpu_baseline(name, T_sample=16384, min_seconds=8.0):
+    """The oracle's decode step (standard MHA over explicit float64 K and V)
+    on one sequence of T_sample tokens of the workload's shape, on all the
+    BLAS threads and on one, scaled linearly to the workload's token count."""
     import oracle
     import synthetic as syn
+    from threadpoolctl import threadpool_info, threadpool_limits
     cfg = syn.shrink(syn.CONFIGS[name], B=1, T_max=T_sample, len_lo=T_sample, len_hi=T_sample)
     full = syn.CONFIGS[name]
     wl = syn.make(cfg)
     K = oracle.cache_to_f64(wl.K)
     V = oracle.explicit_values(wl.K, wl.w.W_K, wl.w.W_V)  # plays the role of the prefill: untimed
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = None
-    times = []
-    t_all = time.time()
-    while time.time() - t_all < min_seconds or len(times) < 3:
-        t = time.perf_counter()
-        oracle.mha_decode(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
-        times.append(time.perf_counter() - t)
-    t_med = float(np.median(times))
-    # the oracle's decode work is linear in the live tokens: scale to the full workload
+
+    def run():
+        times = []
+        t_all = time.time()
+        while time.time() - t_all < min_seconds or len(times) < 3:
+            t = time.perf_counter()
+            oracle.mha_decode(wl.q, K, V, wl.lengths, cfg.H, cfg.dh, cfg.scale)
+            times.append(time.perf_counter() - t)
+        return float(np.median(times)), len(times)
+
     full_tokens = int(syn.lengths(full).astype(np.int64).sum())
-    t_step = t_med * full_tokens / T_sample
-    cpu_model = platform.processor() or ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    info = threadpool_info()
+    threads = max((i.get("num_threads") or 1) for i in info) if info else 1
+    t_all, n_all = run()
+    with threadpool_limits(1):
+        t_one, n_one = run()
+    scale = full_tokens / T_sample
+    sample = (f"float64 numpy oracle (standard MHA over explicit K and V) on one sequence of {T_sample} tokens "
+              f"of the {name} shape (d={full.d}, H={full.H}, dh={full.dh}), median of {{}} runs ({{:.1f}} ms), "
+              f"scaled linearly to {full_tokens} tokens; V construction untimed")
     return {
-        "value": full.B / t_step,
-        "unit": "tokens/s",
-        "cores": threads if threads else os.cpu_count(),
-        "kind": "oracle",
-        "sample": (f"float64 numpy oracle (standard MHA over explicit K and V) on one sequence of "
-                   f"{T_sample} tokens of the {name} shape (d={full.d}, H={full.H}, dh={full.dh}), "
-                   f"median of {len(times)} runs ({t_med * 1e3:.1f} ms), scaled linearly to "
-                   f"{full_tokens} tokens; V construction untimed"),
-        "host_cpus": os.cpu_count(),
-        "cpu_model": cpu_model,
+        "value": full.B / (t_all * scale), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": sample.format(n_all, t_all * 1e3),
+        "single_thread": {"value": full.B / (t_one * scale), "unit": "tokens/s", "cores": 1,
+                          "sample": sample.format(n_one, t_one * 1e3)},
+        "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
     }
 
 
@@ -401,22 +448,16 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    extras = not args.no_extras
 
     name = args.config
-    wl = Workload(name, torch, slim, with_v=not args.no_extras)
+    wl = Workload(name, torch, slim, with_v=extras)
     cfg = wl.cfg
-    log(f"[bench] timing {name}: {args.warmup} warmup + {args.steps} steps")
-    ms_step, attend = time_slim(wl, torch, slim, args.steps, args.warmup)
-    att_ms = float(attend.mean())
-    tokens_s = cfg.B / (ms_step * 1e-3)
-    k_gbps_step = wl.k_bytes / (ms_step * 1e-3) / 1e9
-    k_gbps_attend = wl.k_bytes / (att_ms * 1e-3) / 1e9
-    log(f"[bench] {name}: {ms_step * 1e3:.1f} us/step, attend {att_ms * 1e3:.1f} us "
-        f"({k_gbps_attend:.0f} GB/s), step K-rate {k_gbps_step:.0f} GB/s, {tokens_s:.1f} tokens/s")
-
+    head = decode_record(wl, torch, slim, args.steps, args.warmup, with_kv=extras)
+    ms_step = head["ms_per_step"]
     res = {
         "metric": METRIC,
-        "value": tokens_s,
+        "value": head["tokens_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -425,58 +466,59 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if cfg.cache == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.desc, "d": cfg.d, "H": cfg.H, "dh": cfg.dh, "batch": cfg.B,
-                   "T": cfg.T_max, "k_cache": "bf16", "w_kv": cfg.wkv,
+                   "T": cfg.T_max, "k_cache": cfg.cache, "w_kv": cfg.wkv,
                    "arith": "fp32 scores/softmax/accumulate, bf16 softmax-times-K on MFMA"},
-        "k_cache_gbps": k_gbps_step,
-        "k_cache_hbm_frac": k_gbps_step / HBM_PEAK_GBPS,
-        "roofline": {"bound": "hbm", "achieved": k_gbps_attend, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": k_gbps_attend / HBM_PEAK_GBPS,
+        "k_cache_gbps": head["k_cache_gbps"],
+        "k_cache_hbm_frac": head["k_cache_hbm_frac"],
+        "roofline": {"bound": "hbm", "achieved": head["attend_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": head["attend_gbps"] / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(ATTEND_SOURCES) if name == "long_128k" else None,
-                     "kernel": attend_kernel_name(cfg), "kernel_us": att_ms * 1e3,
+                     "kernel": head["attend_kernel"], "kernel_us": head["attend_us"]["mean"],
                      "algorithmic_bytes": wl.k_bytes},
+        "decode": head,
     }
 
-    if not args.no_extras:
-        ms_gen = time_step(wl, torch, slim, max(10, args.steps // 2), 3)
-        wbytes = 2 * cfg.d * cfg.d * 2
+    if extras:
+        ms_gen = time_step(wl, torch, slim, args.steps, 3)
         res["generation_step"] = {
             "what": ("slim_step: q = x.W_Q and k = x.W_K (bf16 weights, fp32 accumulate), attention "
                      "over len_b - 1 cached rows, k appended at row len_b - 1"),
             "tokens_s": cfg.B / (ms_gen * 1e-3), "ms_per_step": ms_gen,
             "over_decode_us": (ms_gen - ms_step) * 1e3,
-            "projection_weight_bytes": wbytes}
-        log(f"[bench] generation step: {ms_gen * 1e3:.1f} us/step "
-            f"({(ms_gen - ms_step) * 1e3:.1f} us over the decode)")
-        res["multi_query"] = time_multi(torch, slim, max(10, args.steps // 2))
-        ms_kv = time_kv(wl, torch, slim, max(10, args.steps // 2), 3)
-        res["comparator"] = {"what": "standard MHA decode over explicit bf16 K and V caches (same box)",
-                             "tokens_s": cfg.B / (ms_kv * 1e-3), "ms_per_step": ms_kv,
-                             "kv_gbps": 2 * wl.k_bytes / (ms_kv * 1e-3) / 1e9,
-                             "slim_speedup": ms_kv / ms_step}
-        log(f"[bench] comparator: {ms_kv * 1e3:.1f} us/step, slim speedup {ms_kv / ms_step:.2f}x")
+            "projection_weight_bytes": 2 * cfg.d * cfg.d * 2}
+        log(f"[bench] generation step: {ms_gen * 1e3:.1f} us/step ({(ms_gen - ms_step) * 1e3:.1f} us over the decode)")
         res["probe_read_gbps"] = probe_read_gbps(torch, slim, wl.K[0])
         log(f"[bench] HBM read probe: {res['probe_read_gbps']:.0f} GB/s")
         res["probe_copy_gbps"] = probe_copy_gbps(torch, slim, wl.K[1], wl.K[0])
         log(f"[bench] HBM copy probe (read+write): {res['probe_copy_gbps']:.0f} GB/s")
-        del wl
+        res["multi_query"] = time_multi(torch, slim, args.steps)
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    shapes = SHAPES if args.shapes == "all" else ([] if args.shapes == "none" else args.shapes.split(","))
+    res["shapes"] = {}
+    for s in shapes:
+        if s == name:
+            continue
+        w2 = Workload(s, torch, slim, with_v=extras)
+        res["shapes"][s] = decode_record(w2, torch, slim, args.steps, args.warmup, with_kv=extras)
+        del w2
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        if name == "long_128k":
-            w2 = Workload("7b_8k", torch, slim, with_v=False)
-            ms2, att2 = time_slim(w2, torch, slim, max(10, args.steps // 2), 3)
-            res["secondary"] = {"workload": w2.cfg.desc, "tokens_s": w2.cfg.B / (ms2 * 1e-3),
-                                "ms_per_step": ms2, "k_cache_gbps": w2.k_bytes / (ms2 * 1e-3) / 1e9,
-                                "attend_gbps": w2.k_bytes / (att2.mean() * 1e-3) / 1e9}
-            log(f"[bench] 7b_8k: {ms2 * 1e3:.1f} us/step, {res['secondary']['k_cache_gbps']:.0f} GB/s")
-            del w2
-            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
+        log("[bench] cpu baseline (oracle, all threads and one thread) ...")
         res["cpu_baseline"] = cpu_baseline(name)
-        log(f"[bench] cpu baseline: {res['cpu_baseline']['value']:.3f} tokens/s")
+        log(f"[bench] cpu baseline: {res['cpu_baseline']['value']:.3f} tokens/s on {res['cpu_baseline']['cores']} "
+            f"threads, {res['cpu_baseline']['single_thread']['value']:.3f} on one")
+    # release device memory explicitly before the interpreter's exit handlers run
+    torch.cuda.synchronize()
+    _WEIGHTS.clear()
+    torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 
