@@ -119,7 +119,9 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
  *             slim_decode_workspace_bytes(B, H, dh, T_max, k_dt) bytes,
  *             16-byte aligned; its contents on entry do not matter.
  * Arithmetic: scores, softmax and all accumulation in float32; for bf16 caches
- * the softmax weights are rounded to bf16 for the MFMA contraction with K.
+ * the softmax weights are rounded to bf16 for the MFMA contraction with K,
+ * and each token chunk's partial (softmax-times-K sums, accumulated in fp32)
+ * is rounded to bf16 once when stored for the merge.
  * Supported: k_dt bf16 (MFMA path: H <= 32, dh in {32, 64, 128}, d % 8 == 0)
  * or f32 (H <= 64, any dh); w_dt f32 or bf16; B <= 4096.
  * Alignment: K_cache, W_KV and workspace 16 bytes; q, lengths, out 4 bytes.
@@ -144,6 +146,9 @@ size_t slim_decode_workspace_bytes(int B, int H, int dh, int T_max, slim_dtype_t
  * attend phase cuts the rows into (the workspace size follows it, so query
  * slim_decode_workspace_bytes with the same setting); SLIM_XCHG=0 turns off
  * the score-exchange kernel.  Results agree to rounding with the defaults.
+ * SLIM_PARTIALS=f32 keeps the chunk partials of bf16 caches in fp32 (by
+ * default they are rounded once to bf16 when stored; every accumulation is
+ * fp32 either way; query slim_decode_workspace_bytes with the same setting).
  * SLIM_XCHG_SPIN=n bounds each exchange wait to n re-polls, and
  * SLIM_XCHG_SKEW=1 makes one column group's entries never match, so that
  * every wait runs out (failure-path tests).

@@ -97,8 +97,12 @@ bool make_decode_plan(int B, int H, int dh, int T_max, bool bf16_k, int ncu, Dec
   p->off_status = 0;
   p->off_tickets = 8;
   size_t off = 256;
+  // bf16 caches keep their chunk partials in bf16 (accumulated in fp32,
+  // rounded once when stored); SLIM_PARTIALS=f32 keeps them in fp32
+  const char* pe = std::getenv("SLIM_PARTIALS");
+  p->ubf16 = bf16_k && !(pe && std::strcmp(pe, "f32") == 0);
   p->off_U = off;
-  off += align256((size_t)p->nslots * H * d * sizeof(float));
+  off += align256((size_t)p->nslots * H * d * (p->ubf16 ? 2 : 4));
   p->off_ml = off;
   off += align256((size_t)p->nslots * 2 * H * sizeof(float));
   p->off_op = off;

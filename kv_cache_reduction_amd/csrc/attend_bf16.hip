@@ -57,10 +57,11 @@ struct AttendBf16Params {
   const float* q;
   const uint16_t* K;
   const int32_t* lengths;
-  float* U;
+  void* U;           // partials: bf16 (ubf16) or fp32
   float* ml;
   uint32_t* status;  // cleared here; the finish sets it if a piece is marked failed
   int B, H, d, T_max, nch, dc, nslots;
+  bool ubf16;
   float qscale;
 };
 
@@ -173,6 +174,32 @@ __device__ __forceinline__ void halves(float x, float& a, float& b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   a = __uint_as_float(r[0]);
   b = __uint_as_float(r[1]);
+}
+
+// A piece's partials: MFMA s, lane l, element e holds head
+// 8*(e/4) + 4*(l/32) + e%4 at unit column 32s + l%32; columns at or past
+// `clim` are not stored.  bf16 partials are rounded to nearest even once,
+// here; the accumulation before and the merge after are fp32.
+__device__ __forceinline__ void store_partials(const AttendBf16Params& p, const f32x16 (&acc)[8], int slot, int col,
+                                               int clim, int half) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+    if (row < p.H) {
+      const size_t base = ((size_t)row * p.nslots + slot) * p.d + col;
+      if (p.ubf16) {
+        __bf16* dst = static_cast<__bf16*>(p.U) + base;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (col + 32 * s < clim) dst[32 * s] = (__bf16)acc[s][e];
+      } else {
+        float* dst = static_cast<float*>(p.U) + base;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (col + 32 * s < clim) dst[32 * s] = acc[s][e];
+      }
+    }
+  }
 }
 
 template <int DH, int GC, int NST>
@@ -400,16 +427,7 @@ __global__ void __launch_bounds__(512) attend_bf16_kernel(AttendBf16Params p) {
     // 8*(e/4) + 4*(l/32) + e%4 at unit column 32s + l%32
     float la, lb;
     halves(l_half, la, lb);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * half + (e & 3);
-      if (row < p.H) {
-        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ubase + l32;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          if (ubase + 32 * s + l32 < clim) dst[32 * s] = acc[s][e];
-      }
-    }
+    store_partials(p, acc, slot, ubase + l32, clim, half);
     if (cg == 0 && wave == 0 && lane < p.H) {
       p.ml[(size_t)slot * 2 * p.H + lane] = m_ref;
       p.ml[(size_t)slot * 2 * p.H + p.H + lane] = la + lb;
@@ -722,15 +740,7 @@ __global__ void __launch_bounds__(512) attend_xchg_kernel(XchgParams xp) {
 
     float la, lb;
     halves(l_half, la, lb);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = 8 * (e >> 2) + 4 * half + (e & 3);
-      if (row < p.H) {
-        float* dst = p.U + ((size_t)row * p.nslots + slot) * d + ubase + l32;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) dst[32 * s] = acc[s][e];
-      }
-    }
+    store_partials(p, acc, slot, ubase + l32, d, half);
     if (cg == 0 && wave == 0 && lane < p.H) {
       p.ml[(size_t)slot * 2 * p.H + lane] = failed ? __uint_as_float(kQuietNaN) : m_ref;
       p.ml[(size_t)slot * 2 * p.H + p.H + lane] = la + lb;
@@ -746,7 +756,8 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_
   p.q = a.q;
   p.K = static_cast<const uint16_t*>(a.K);
   p.lengths = a.lengths;
-  p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
+  p.U = a.ws + pl.off_U;
+  p.ubf16 = pl.ubf16;
   p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
   p.status = a.status;
   p.B = a.B;
@@ -803,7 +814,8 @@ static hipError_t launch_xchg(const DecodePlan& pl, const DecodeArgs& a, hipStre
   p.q = a.q;
   p.K = static_cast<const uint16_t*>(a.K);
   p.lengths = a.lengths;
-  p.U = reinterpret_cast<float*>(a.ws + pl.off_U);
+  p.U = a.ws + pl.off_U;
+  p.ubf16 = pl.ubf16;
   p.ml = reinterpret_cast<float*>(a.ws + pl.off_ml);
   p.status = a.status;
   p.B = a.B;

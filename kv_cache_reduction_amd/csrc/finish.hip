@@ -35,7 +35,7 @@
 
 namespace slim {
 
-constexpr int kMergeBatch = 4;  // slots whose loads a thread issues together
+constexpr int kMergeBatch = 8;  // slots whose loads a thread issues together
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // x = hi + mid + lo exactly, each a bf16 (its bits in the low 16 bits of the
@@ -51,9 +51,9 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
   lo = __float_as_uint(r2) >> 16;
 }
 
-template <int DH, bool WBF16, int PR, bool MFMA>
+template <int DH, bool WBF16, int PR, bool MFMA, bool UB>
 __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __restrict__ lengths,
-                                                            const float* __restrict__ U,
+                                                            const void* __restrict__ Uv,
                                                             const float* __restrict__ ml,
                                                             const void* __restrict__ W,
                                                             float* __restrict__ part,
@@ -157,29 +157,40 @@ __global__ void __launch_bounds__(256) merge_project_kernel(const int32_t* __res
         slot0 = cf + b;
       }
       const bool cols = 4 * c4 < nr;
-      const float* src = U + ((size_t)h * nslots + slot0) * d + r0 + 4 * c4;
       const float* mls = ml + (size_t)slot0 * 2 * H + h;
       for (int i = ss; i < ns; i += kMergeBatch * nss) {  // a batch of slots per round, loads first
+        // every load of the batch is issued unconditionally (slots past the
+        // sequence clamped to its last one, columns past the block to the
+        // first) so that all are in flight together; dead ones are zeroed
+        // after
         float4 x[kMergeBatch];
         float ms[kMergeBatch], ls[kMergeBatch];
+        const size_t col = (size_t)h * nslots * d + (size_t)slot0 * d + r0 + 4 * (cols ? c4 : 0);
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
           const int j = i + k * nss;
-          const bool ok = j < ns;
-          ms[k] = ok ? mls[(size_t)j * 2 * H] : kNegInf;
-          ls[k] = ok ? mls[(size_t)j * 2 * H + H] : 0.f;
-          x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (ok && cols) {
-            const float* v = src + (size_t)j * d;
-            if (aligned) {
-              x[k] = *reinterpret_cast<const float4*>(v);
-            } else {  // rows not 16-byte aligned (d % 4 != 0)
-              x[k].x = v[0];
-              if (4 * c4 + 1 < nr) x[k].y = v[1];
-              if (4 * c4 + 2 < nr) x[k].z = v[2];
-              if (4 * c4 + 3 < nr) x[k].w = v[3];
-            }
+          const int jj = j < ns ? j : ns - 1;
+          ms[k] = mls[(size_t)jj * 2 * H];
+          ls[k] = mls[(size_t)jj * 2 * H + H];
+          if constexpr (UB) {  // bf16 partials (d % 8 == 0: 8-byte aligned)
+            const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Uv) + col + (size_t)jj * d);
+            x[k] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+          } else if (aligned) {
+            x[k] = *reinterpret_cast<const float4*>(static_cast<const float*>(Uv) + col + (size_t)jj * d);
+          } else {  // rows not 16-byte aligned (d % 4 != 0)
+            const float* v = static_cast<const float*>(Uv) + col + (size_t)jj * d;
+            x[k].x = v[0];
+            x[k].y = 4 * c4 + 1 < nr ? v[1] : 0.f;
+            x[k].z = 4 * c4 + 2 < nr ? v[2] : 0.f;
+            x[k].w = 4 * c4 + 3 < nr ? v[3] : 0.f;
           }
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          const bool ok = i + k * nss < ns;
+          ms[k] = ok ? ms[k] : kNegInf;
+          ls[k] = ok ? ls[k] : 0.f;
+          x[k] = ok && cols ? x[k] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) bad |= ms[k] != ms[k];  // an attend piece marked NaN
@@ -342,7 +353,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   constexpr int NRS = 256 / JQ;
   constexpr int NSS = 256 / (PR / 4);
   constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
-  const float* U = reinterpret_cast<const float*>(a.ws + pl.off_U);
+  const void* U = a.ws + pl.off_U;
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
   float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
   const int spw = pl.spw == 16 ? 16 : 8;
@@ -353,12 +364,21 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   const size_t lds =
       (8 + (size_t)RED + (size_t)spw * PR + 2 * NSS + WL + (fixed_ns > 0 ? 0 : (size_t)a.B + 1)) * 4;
   const dim3 grid(a.H, pl.npc, (a.B + spw - 1) / spw);
-  if (mp)
-    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, MFMA_OK>), grid, dim3(256), lds, s, a.lengths, U, ml,
-                       a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+  // bf16 partials exist only for the bf16-cache head widths
+  constexpr bool UB_OK = DH == 32 || DH == 64 || DH == 128;
+  const bool ub = UB_OK && pl.ubf16;
+  if (mp && ub)
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, MFMA_OK, UB_OK>), grid, dim3(256), lds, s, a.lengths, U,
+                       ml, a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+  else if (mp)
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, MFMA_OK, false>), grid, dim3(256), lds, s, a.lengths, U,
+                       ml, a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+  else if (ub)
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false, UB_OK>), grid, dim3(256), lds, s, a.lengths, U,
+                       ml, a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   else
-    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false>), grid, dim3(256), lds, s, a.lengths, U, ml,
-                       a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
+    hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false, false>), grid, dim3(256), lds, s, a.lengths, U,
+                       ml, a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = a.B * a.H * DH;

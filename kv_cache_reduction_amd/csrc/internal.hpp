@@ -21,7 +21,8 @@ struct DecodePlan {
   int proj_rows;   // W_KV rows per finish workgroup (proj_rows(dh, large or not))
   int spw;         // sequences per finish workgroup (finish_seqs)
   int npc;         // W_KV row blocks of the finish (proj_rows rows each)
-  size_t off_U;    // [H, nslots, d] float: unnormalised softmax.K rows per chunk
+  bool ubf16;      // partials U stored in bf16 (bf16 caches), else fp32
+  size_t off_U;    // [H, nslots, d] bf16 or float: unnormalised softmax.K rows per chunk
   size_t off_ml;   // [nslots, 2, H] float (running max in log2 units, normaliser)
   size_t off_op;   // [npc, B, H, dh] float (per-row-block projection partials)
   bool xchg;       // two equal column groups whose workgroups exchange scores

@@ -331,3 +331,26 @@ def test_finish_mfma_projection_f32_cache_bf16_wkv(H, dh):
     o = gpu_decode(cfg, wl.q, to_dev(K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
     ref = oracle_decode(cfg, wl.q, K, wl.lengths, wl.w.W_K, wl.w.W_V)
     _check(f"f32 cache, bf16 W_KV, dh={dh}", o, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("name,kw", [("7b_ragged", dict(B=5, T_max=2000, len_lo=1, len_hi=2000)),
+                                     ("long_128k", dict(T_max=8192)), ("whisper_large", dict(B=5, T_max=700))])
+def test_partials_bf16_and_f32(monkeypatch, name, kw):
+    """bf16 caches keep their chunk partials in bf16 by default (rounded once
+    from the fp32 accumulator); SLIM_PARTIALS=f32 keeps them in fp32.  Both
+    meet the oracle bound, and they differ by about the bf16 rounding of one
+    partial."""
+    import kv_cache_reduction_amd as slim
+    cfg = syn.shrink(syn.CONFIGS[name], **kw)
+    wl = syn.make(cfg)
+    W = dev_wkv(cfg, wl.w.W_K, wl.w.W_V)
+    ref = oracle_decode(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    o16 = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, W)
+    monkeypatch.setenv("SLIM_PARTIALS", "f32")
+    ws = slim.workspace(slim.decode_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, 1))
+    o32 = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, W, ws=ws)
+    e16 = _check(f"{name} bf16 partials", o16, ref, TOL["bf16"])
+    e32 = _check(f"{name} fp32 partials", o32, ref, TOL["bf16"])
+    diff = oracle.err_rel(o16, o32)
+    log(f"[parity] {name}: bf16 vs fp32 partials differ by {diff:.2e} (errors {e16:.2e} / {e32:.2e})")
+    assert diff <= 2.0 ** -7

@@ -46,7 +46,7 @@ def test_noalloc_two_calls_second_smaller():
 def test_noalloc_rejects_a_workspace_over_the_array():
     import torch
     import kv_cache_reduction_amd as slim
-    B, H, dh, T = 64, 32, 128, 8192
+    B, H, dh, T = 512, 32, 128, 8192
     need = slim.decode_workspace_bytes(B, H, dh, T, torch.bfloat16)
     assert need > slim.NOALLOC_SCRATCH_BYTES
     d = H * dh
