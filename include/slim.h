@@ -284,9 +284,10 @@ slim_status_t slim_step(const float* x,
  *               out[i,h,:] = softmax_t(scale * Q[i,h-cols] . K[t,h-cols]) . K[t,:] . W_KV[:, h-cols]
  *   option  : 1 (form V = K.W_KV in the workspace, rounded to bf16, then the
  *             softmax times V), 2 (softmax times K on all d columns, then
- *             W_KV), 0 = the cheaper by multiply-accumulate count:
- *             option 1 costs T d^2 + n T d, option 2 n H T d + n d^2
- *             (slim_multi_query_option returns the choice).
+ *             W_KV), 0 = the cheaper by multiply-accumulate count, with
+ *             option 1's dense V product weighted by 2/3 for its higher rate
+ *             on this device: option 1 costs (2/3) T d^2 + n T d, option 2
+ *             n H T d + n d^2 (slim_multi_query_option returns the choice).
  *   workspace : at least slim_multi_query_workspace_bytes(...) bytes for the
  *             same shape and option, 16-byte aligned.
  * Arithmetic: scores on bf16 MFMA with Q split into high and low bf16 parts

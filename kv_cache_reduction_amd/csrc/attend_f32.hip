@@ -3,10 +3,13 @@
 // and partial format as the bf16 MFMA path, so the finish phase is shared.
 //
 // One workgroup of 256 threads per (token chunk, block of 256 columns of K).
-// Per token: the row is staged in LDS; thread h < H forms the score of head
-// h (log2 units) and updates its running max / normaliser; then thread t
-// updates the accumulator column cb*256 + t of every head:
+// Rows are staged in LDS RB at a time (one load round per block, not per
+// token).  Per block: thread (r, h) forms the score of row r for head h (log2
+// units); thread h < H then walks the block's rows in order, updating its
+// running max and normaliser and recording (alpha, p) per row; then thread t
+// updates the accumulator column cb*256 + t of every head, row by row:
 //   U[h, col] = alpha_h * U[h, col] + p_h * K[t, col].
+// The per-row arithmetic and its order are those of a token-at-a-time loop.
 // Every workgroup recomputes the scores of all heads (each needs all d
 // columns of the row); this path serves small fp32 problems.
 #include <atomic>
@@ -24,7 +27,7 @@ struct AttendF32Params {
   float* U;
   float* ml;
   uint32_t* status;  // cleared here; the finish sets it if a piece is marked failed
-  int B, H, dh, d, T_max, nch, gcf, nslots;
+  int B, H, dh, d, T_max, nch, gcf, nslots, rb;
   float qscale;
 };
 
@@ -32,10 +35,13 @@ constexpr int kF32MaxHeads = 64;
 
 __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
   extern __shared__ int smem[];
+  const int RB = p.rb;
   int* tmp = smem;                                        // [4]
-  float* ap = reinterpret_cast<float*>(smem + 4);         // [2][kF32MaxHeads] alpha, p
-  float* row = ap + 2 * kF32MaxHeads;                     // [d]
-  int* pre = reinterpret_cast<int*>(row + p.d);           // [B + 1]
+  float* qs = reinterpret_cast<float*>(smem + 4);         // [d] the piece's query
+  float* rows = qs + p.d;                                 // [RB][d]
+  float* sc = rows + (size_t)RB * p.d;                    // [RB][H] scores, then weights p
+  float* al = sc + RB * p.H;                              // [RB][H] rescale factors
+  int* pre = reinterpret_cast<int*>(al + RB * p.H);       // [B + 1]
 
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && tid == 0) *p.status = 0u;
@@ -56,35 +62,45 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
     if (s1 == s0) continue;
     const int tb = max(cbeg, s0) - s0, te = min(cend, s1) - s0;
     const int slot = c + b;
-    const float* qb = p.q + (size_t)b * p.d;
+    for (int i = tid; i < p.d; i += 256) qs[i] = p.q[(size_t)b * p.d + i];
 
     float m = kNegInf, l = 0.f;  // head tid (tid < H)
     float acc[kF32MaxHeads];
 #pragma unroll
     for (int h = 0; h < kF32MaxHeads; ++h) acc[h] = 0.f;
 
-    for (int t = tb; t < te; ++t) {
-      const float* kr = p.K + ((size_t)b * p.T_max + t) * p.d;
-      for (int i = tid; i < p.d; i += 256) row[i] = kr[i];
+    for (int t0 = tb; t0 < te; t0 += RB) {
+      const int nr = min(RB, te - t0);
+      const float* kr = p.K + ((size_t)b * p.T_max + t0) * p.d;
+      for (int i = tid; i < nr * p.d; i += 256) rows[i] = kr[i];
+      __syncthreads();
+      for (int i = tid; i < nr * p.H; i += 256) {
+        const int r = i / p.H, h = i % p.H;
+        float s = 0.f;
+        for (int j = 0; j < p.dh; ++j) s = fmaf(qs[h * p.dh + j], rows[(size_t)r * p.d + h * p.dh + j], s);
+        sc[i] = s * p.qscale;
+      }
       __syncthreads();
       if (tid < p.H) {
-        float s = 0.f;
-        for (int j = 0; j < p.dh; ++j) s = fmaf(qb[tid * p.dh + j], row[tid * p.dh + j], s);
-        s *= p.qscale;
-        const float m_new = fmaxf(m, s);
-        const float a = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
-        const float e = (m_new == kNegInf) ? 0.f : fast_exp2(s - m_new);
-        l = a * l + e;
-        m = m_new;
-        ap[tid] = a;
-        ap[kF32MaxHeads + tid] = e;
+        for (int r = 0; r < nr; ++r) {
+          const float s = sc[r * p.H + tid];
+          const float m_new = fmaxf(m, s);
+          const float a = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
+          const float e = (m_new == kNegInf) ? 0.f : fast_exp2(s - m_new);
+          l = a * l + e;
+          m = m_new;
+          al[r * p.H + tid] = a;
+          sc[r * p.H + tid] = e;
+        }
       }
       __syncthreads();
       if (col_ok) {
-        const float kv = row[col];
+        for (int r = 0; r < nr; ++r) {
+          const float kv = rows[(size_t)r * p.d + col];
 #pragma unroll
-        for (int h = 0; h < kF32MaxHeads; ++h)
-          if (h < p.H) acc[h] = fmaf(ap[kF32MaxHeads + h], kv, ap[h] * acc[h]);
+          for (int h = 0; h < kF32MaxHeads; ++h)
+            if (h < p.H) acc[h] = fmaf(sc[r * p.H + h], kv, al[r * p.H + h] * acc[h]);
+        }
       }
       __syncthreads();
     }
@@ -117,7 +133,13 @@ hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStrea
   p.gcf = pl.gc;
   p.nslots = pl.nslots;
   p.qscale = a.scale * kLog2e;
-  const size_t lds = (4 + 2 * kF32MaxHeads + (size_t)a.d + (size_t)a.B + 1) * 4;
+  // rows per LDS block: at most 64, 32 KB of rows and 2048 (row, head) pairs
+  int rb = 32768 / (4 * a.d);
+  if (rb > 64) rb = 64;
+  if (rb > 2048 / a.H) rb = 2048 / a.H;
+  if (rb < 1) rb = 1;
+  p.rb = rb;
+  const size_t lds = (4 + (size_t)a.d + (size_t)rb * a.d + 2 * (size_t)rb * a.H + (size_t)a.B + 1) * 4;
   static std::atomic<int> granted[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(attend_f32_kernel), lds, granted);
   if (e != hipSuccess) return e;

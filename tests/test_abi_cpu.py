@@ -198,8 +198,21 @@ def test_multi_query_rejects_bad_arguments(slim):
                                    (63, 20, 64, 1500), (66, 20, 64, 1500), (5, 2, 64, 7), (300, 32, 128, 512)])
 def test_multi_query_option_follows_the_cost_model(slim, shape):
     """The library's option choice is the cheaper option by the multiply-
-    accumulate counts the oracle states (ties go to option 2)."""
+    accumulate counts the oracle states, with option 1's dense V product
+    (T d^2 of its count) weighted by 2/3 as the header documents (ties go to
+    option 2)."""
     n, H, dh, T = shape
-    c = oracle.multi_query_cost(n, H, T, H * dh)
-    want = 1 if c["opt1"] < c["opt2"] else 2
+    d = H * dh
+    c = oracle.multi_query_cost(n, H, T, d)
+    want = 1 if c["opt1"] - T * d * d / 3.0 < c["opt2"] else 2
     assert slim.multi_query_option(n, H, dh, T) == want
+
+
+def test_multi_query_option_picks_option1_for_the_whisper_shared_context(slim):
+    """64 decoder queries over a 1500-row encoder context (d=1280, H=20): the
+    pure counts are within 1% of each other (option 2 by a hair), the dense
+    V product makes option 1 the faster one."""
+    c = oracle.multi_query_cost(64, 20, 1500, 1280)
+    assert c["opt2"] < c["opt1"] < 1.01 * c["opt2"]
+    assert slim.multi_query_option(64, 20, 64, 1500) == 1
+    assert slim.multi_query_option(1, 32, 128, 131072) == 2
