@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--shapes", default="all", help="comma list of other workloads to time, 'all' or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip generation step, many queries, comparators, probes")
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="only time the CPU oracle on every decode workload (bounded samples) and print one JSON line")
     return ap.parse_args()
 
 
@@ -394,7 +396,23 @@ def _cpu_model():
     return platform.processor() or ""
 
 
-def cpu_baseline(name, T_sample=16384, min_seconds=8.0):
+def cpu_all(min_seconds=4.0):
+    """The oracle's decode step on a bounded sample of every workload (all BLAS
+    threads), scaled linearly to the workload's token count."""
+    import synthetic as syn
+    out = {}
+    for name in ["long_128k"] + SHAPES:
+        full = syn.CONFIGS[name]
+        tokens = int(syn.lengths(full).astype(np.int64).sum())
+        T = int(min(16384, max(1, tokens // full.B)))
+        rec = cpu_baseline(name, T_sample=T, min_seconds=min_seconds, single=False)
+        out[name] = {"tokens_s": rec["value"], "ms_per_step": full.B / rec["value"] * 1e3, "cores": rec["cores"],
+                     "sample": rec["sample"]}
+        log(f"[bench] cpu oracle {name}: {rec['value']:.2f} tokens/s ({full.B / rec['value'] * 1e3:.1f} ms per step)")
+    return out
+
+
+def cpu_baseline(name, T_sample=16384, min_seconds=8.0, single=True):
     """The oracle's decode step (standard MHA over explicit float64 K and V)
     on one sequence of T_sample tokens of the workload's shape, on all the
     BLAS threads and on one, scaled linearly to the workload's token count."""
@@ -420,8 +438,10 @@ def cpu_baseline(name, T_sample=16384, min_seconds=8.0):
     info = threadpool_info()
     threads = max((i.get("num_threads") or 1) for i in info) if info else 1
     t_all, n_all = run()
-    with threadpool_limits(1):
-        t_one, n_one = run()
+    t_one, n_one = t_all, n_all
+    if single:
+        with threadpool_limits(1):
+            t_one, n_one = run()
     scale = full_tokens / T_sample
     sample = (f"float64 numpy oracle (standard MHA over explicit K and V) on one sequence of {T_sample} tokens "
               f"of the {name} shape (d={full.d}, H={full.H}, dh={full.dh}), median of {{}} runs ({{:.1f}} ms), "
@@ -443,6 +463,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path's sharding over "
               f"several GPUs is a design, not built or run here", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_all:
+        print(json.dumps({"cpu_oracle": cpu_all(), "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}), flush=True)
+        return
     import torch
     import kv_cache_reduction_amd as slim
     assert torch.cuda.is_available(), "no GPU visible"
