@@ -7,17 +7,18 @@
 //
 // multi_attend<DH, QW, OPT>  grid (column blocks, H x query groups, T splits),
 // QW waves of 64 lanes; wave w owns 32 queries of head h.
-//  * Tiles of 32 context rows travel global -> registers -> LDS (double
-//    buffered, one barrier per tile): head h's DH key columns for the scores
+//  * Tiles of 32 context rows travel global -> registers -> LDS (two tiles
+//    in flight in registers while a third is used from LDS; two LDS
+//    buffers, one barrier per tile): head h's DH key columns for the scores
 //    and the value block: 128 columns of K (option 2) or head h's DH columns
 //    of V (option 1).  All waves of the workgroup share the tile.
-//  * Scores on 32x32x8 bf16 MFMA, computed transposed (S^T = K_h . Q_h^T,
+//  * Scores on 32x32x16 bf16 MFMA, computed transposed (S^T = K_h . Q_h^T,
 //    the tile's K rows as the A operand, Q as the B operand) with Q split
 //    into bf16 high and low parts (two MFMAs per step), so the products keep
 //    about 16 bits of Q; fp32 accumulation.  The reduction over the head's
-//    DH dimensions is ordered so that a lane's A operand is one 8-byte LDS
+//    DH dimensions is ordered so that a lane's A operand is one 16-byte LDS
 //    read of its row: lanes 0-31 take dimensions [0, DH/2), lanes 32-63
-//    [DH/2, DH), four per step, and Q (in registers for the whole kernel)
+//    [DH/2, DH), eight per step, and Q (in registers for the whole kernel)
 //    follows the same order.
 //  * The transposed result already has the A-operand layout of P . V (lane =
 //    query, 16 context rows each, halves joined by a lane swap), where the
@@ -25,8 +26,11 @@
 //    a reference max m (log2 units; Q is pre-scaled by scale*log2 e) that
 //    moves only when a score exceeds it by more than 8, so weights stay
 //    below 2^8; the accumulator rows are then rescaled through LDS.
-//  * P (bf16) . value block on 32x32x8 MFMA, B operands by transpose reads
-//    (ds_read_b64_tr_b16) of the tile rows.
+//  * P (bf16) . value block on 32x32x16 MFMA, each B operand from two
+//    transpose reads (ds_read_b64_tr_b16) of the tile rows.  A 16-row step
+//    takes, in lane half g, the context rows 4g..4g+3 and 8+4g..8+4g+3 of
+//    its 16 (the order the transposed scores hold them in); the B operand
+//    takes the same rows, and the MFMA sums over them in any order.
 //  * Option 2 writes unnormalised partial rows U[h, q*nsplit + split, cols]
 //    and (column block 0) m and the normaliser l, the layout the decode
 //    finish merges and projects by W_KV.  Option 1 writes the normalised
@@ -114,19 +118,25 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
 
   // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
   // order: step k takes dimensions hh*DH/2 + 4k .. +3
-  s16x4 qh[DH / 8], ql[DH / 8];
+  bf16x8_t qh[DH / 16], ql[DH / 16];
   {
     const float* qr = p.Q + (size_t)(qok ? q : 0) * d + h * DH + hh * (DH / 2);
 #pragma unroll
-    for (int k = 0; k < DH / 8; ++k) {
-      const float4 v = qok ? *reinterpret_cast<const float4*>(qr + 4 * k) : make_float4(0.f, 0.f, 0.f, 0.f);
-      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-      split_bf16(v.x * p.qscale, h0, l0);
-      split_bf16(v.y * p.qscale, h1, l1);
-      split_bf16(v.z * p.qscale, h2, l2);
-      split_bf16(v.w * p.qscale, h3, l3);
-      qh[k] = s16x4{(short)h0, (short)h1, (short)h2, (short)h3};
-      ql[k] = s16x4{(short)l0, (short)l1, (short)l2, (short)l3};
+    for (int k = 0; k < DH / 16; ++k) {
+      s16x4 hv[2], lv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float4 v = qok ? *reinterpret_cast<const float4*>(qr + 8 * k + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_bf16(v.x * p.qscale, h0, l0);
+        split_bf16(v.y * p.qscale, h1, l1);
+        split_bf16(v.z * p.qscale, h2, l2);
+        split_bf16(v.w * p.qscale, h3, l3);
+        hv[e] = s16x4{(short)h0, (short)h1, (short)h2, (short)h3};
+        lv[e] = s16x4{(short)l0, (short)l1, (short)l2, (short)l3};
+      }
+      qh[k] = join_bf16x8(hv[0], hv[1]);
+      ql[k] = join_bf16x8(lv[0], lv[1]);
     }
   }
 
@@ -154,18 +164,21 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
       ch_lds[i] = (uint32_t)(kMTile * S::SP + r * S::VP + 16 * k8);
     }
   }
-  uint4 stage[CPT];
-  auto load_tile = [&](int tb) {
+  uint4 stage[2][CPT];  // tiles it+1 and it+2 in flight while tile it is used
+  auto load_tile = [&](uint4 (&st)[CPT], int tb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int row = min(tb + ch_row[i], p.T - 1);
-      stage[i] = ch_ok[i] ? *reinterpret_cast<const uint4*>(ch_src[i] + (size_t)row * d) : make_uint4(0, 0, 0, 0);
+      // always issued (unused chunks are never stored); loaded as a vector
+      // value, so that the stage stays in registers
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ch_src[i] + (size_t)row * d);
+      st[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
-  auto store_tile = [&](char* buf) {
+  auto store_tile = [&](const uint4 (&st)[CPT], char* buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      if (ch_ok[i]) *reinterpret_cast<uint4*>(buf + ch_lds[i]) = stage[i];
+      if (ch_ok[i]) *reinterpret_cast<uint4*>(buf + ch_lds[i]) = st[i];
   };
 
   float* rv = rowv + wave * 32;
@@ -181,13 +194,17 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   for (int s = 0; s < S::NCT; ++s) acc[s] = f32x16{0};
   float m_ref = kNegInf, l_half = 0.f;
 
-  if (ntiles > 0) load_tile(t_begin);
-  for (int it = 0; it < ntiles; ++it) {
+  // loads are issued unconditionally (rows clamped), so that the compiler
+  // can count the tiles in flight and wait for one tile only
+  load_tile(stage[0], t_begin);
+  load_tile(stage[1], t_begin + kMTile);
+  // one tile: into LDS from its stage, then the stage takes tile it + 2
+  auto tile = [&](int it, uint4 (&st)[CPT]) {
     char* buf = tiles + (it & 1) * S::TILE;
-    store_tile(buf);
+    store_tile(st, buf);
     __syncthreads();
     const int tb = t_begin + it * kMTile;
-    if (it + 1 < ntiles) load_tile(tb + kMTile);
+    load_tile(st, tb + 2 * kMTile);
 
     // scores of the tile, transposed: S^T = K_h . Q_h^T with the K rows as
     // the A operand and Q (registers) as the B operand.  The result layout
@@ -197,10 +214,10 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     {
       const char* srow = buf + m * S::SP + hh * DH;  // context row l%32, this half's dimensions
 #pragma unroll
-      for (int k = 0; k < DH / 8; ++k) {
-        const s16x4 a = *reinterpret_cast<const s16x4*>(srow + 8 * k);
-        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, qh[k], sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, ql[k], sc, 0, 0, 0);
+      for (int k = 0; k < DH / 16; ++k) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(srow + 16 * k);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[k], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[k], sc, 0, 0, 0);
       }
     }
     // rows past a query's limit (or the split) are -inf; only tiles that
@@ -247,18 +264,27 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
       l_half = dot2_bf16(w1, kOnes2, dot2_bf16(w0, kOnes2, l_half));
       pa[k] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
     }
-    // P . value block
+    // P . value block, 16 context rows per MFMA
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const lds_s16x4_m* a0 =
-          (const lds_s16x4_m*)(size_t)((uint32_t)(uintptr_t)(buf + tr_off) + (uint32_t)(8 * k * S::VP));
+    for (int k = 0; k < 2; ++k) {
+      const bf16x8_t a = join_bf16x8(pa[2 * k], pa[2 * k + 1]);
+      const lds_s16x4_m* r0 =
+          (const lds_s16x4_m*)(size_t)((uint32_t)(uintptr_t)(buf + tr_off) + (uint32_t)(16 * k * S::VP));
+      const lds_s16x4_m* r1 =
+          (const lds_s16x4_m*)(size_t)((uint32_t)(uintptr_t)(buf + tr_off) + (uint32_t)((16 * k + 8) * S::VP));
 #pragma unroll
       for (int s = 0; s < S::NCT; ++s) {
-        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_m*>(a0 + 8 * s));
-        acc[s] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(pa[k], b, acc[s], 0, 0, 0);
+        const s16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_m*>(r0 + 8 * s));
+        const s16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_m*>(r1 + 8 * s));
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, join_bf16x8(b0, b1), acc[s], 0, 0, 0);
       }
     }
+  };
+  for (int it = 0; it + 1 < ntiles; it += 2) {
+    tile(it, stage[0]);
+    tile(it + 1, stage[1]);
   }
+  if (ntiles & 1) tile(ntiles - 1, stage[0]);
 
   const float l_row = pair_sum(l_half);
   const int qbase = (qg * QW + wave) * 32;

@@ -31,6 +31,16 @@ def test_7b_ragged_full_size_whole_output():
     _check("7b_ragged", o, ref)
 
 
+def test_7b_8k_full_size_whole_output():
+    cfg = syn.CONFIGS["7b_8k"]
+    log(f"[fullsize] 7b_8k: generating {cfg.desc}")
+    wl = syn.make(cfg)
+    o = gpu_decode(cfg, wl.q, to_dev(wl.K), wl.lengths, dev_wkv(cfg, wl.w.W_K, wl.w.W_V))
+    log("[fullsize] 7b_8k: oracle over all 16 x 32 (sequence, head) pairs")
+    ref = oracle_decode_full(cfg, wl.q, wl.K, wl.lengths, wl.w.W_K, wl.w.W_V)
+    _check("7b_8k", o, ref)
+
+
 def test_long_128k_full_131072_whole_output():
     cfg = syn.CONFIGS["long_128k"]
     log(f"[fullsize] long_128k: generating {cfg.desc}")
