@@ -10,8 +10,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -68,12 +66,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
   hi = f32_to_bf16_rne(x);
   lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
-}
-
-// The 8-element bf16 operand of a 32x32x16 MFMA from two 4-element halves
-// (elements 0-3 from a, 4-7 from b).
-__device__ __forceinline__ bf16x8_t join_bf16x8(s16x4 a, s16x4 b) {
-  return __builtin_bit_cast(bf16x8_t, (s16x8)__builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulation.

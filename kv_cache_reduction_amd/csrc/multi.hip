@@ -37,6 +37,7 @@
 //    output rows directly (one split) or partial rows of the head's dh
 //    columns that multi_merge combines.
 #include "common.hpp"
+#include "mfma16.hpp"
 #include "internal.hpp"
 #include "multi.hpp"
 #include "launch.hpp"

@@ -16,6 +16,7 @@
 // let the younger blocks stay in flight.
 // fp32: a plain LDS-tiled VALU GEMM (64x64 tiles, 4x4 outputs per thread).
 #include "common.hpp"
+#include "mfma16.hpp"
 #include "internal.hpp"
 
 namespace slim {
