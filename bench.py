@@ -169,12 +169,15 @@ def _loop_ms(torch, fn, steps):
 
 
 def time_decode(wl, torch, slim, steps, warmup):
-    """Step time from `steps` back-to-back slim_decode calls; per-step and
-    per-phase distributions from event-bracketed calls."""
+    """Per-step and per-phase distributions from event-bracketed calls, then
+    the step time from `steps` back-to-back slim_decode calls.  The
+    distribution loops run first, after the warm-up: they bring the GPU out
+    of the clock state it idles in while the host builds the inputs (a loop
+    timed straight after a short warm-up runs a few percent slow), so that
+    the timed loop measures the steady state of a decode loop."""
     for i in range(warmup):
         slim.decode(*wl.args(i))
     torch.cuda.synchronize()
-    ms_step = _loop_ms(torch, lambda i: slim.decode(*wl.args(i)), steps)
     n = max(steps, DIST_STEPS)
     E = torch.cuda.Event
     e = [[E(enable_timing=True) for _ in range(n)] for _ in range(3)]
@@ -193,6 +196,8 @@ def time_decode(wl, torch, slim, steps, warmup):
     torch.cuda.synchronize()
     attend_us = np.array([e[0][i].elapsed_time(e[1][i]) for i in range(n)]) * 1e3
     finish_us = np.array([e[1][i].elapsed_time(e[2][i]) for i in range(n)]) * 1e3
+    torch.cuda.synchronize()
+    ms_step = _loop_ms(torch, lambda i: slim.decode(*wl.args(i)), steps)
     st = slim.decode_status(wl.ws)
     if st != 0:
         raise RuntimeError(f"{wl.name}: decode reported status {st}")
@@ -253,17 +258,35 @@ def time_step(wl, torch, slim, steps, warmup):
     row len_b - 1 (the same row every step, so the cache never fills)."""
     import synthetic as syn
     cfg = wl.cfg
-    WQ = dev_bits(torch, syn.f32_to_bf16_bits(wl.w.W_Q.astype(np.float32)))
-    WK = dev_bits(torch, syn.f32_to_bf16_bits(wl.WK.astype(np.float32)))
+    if cfg.cache == "bf16":
+        WQ = dev_bits(torch, syn.f32_to_bf16_bits(wl.w.W_Q.astype(np.float32)))
+        WK = dev_bits(torch, syn.f32_to_bf16_bits(wl.WK.astype(np.float32)))
+    else:  # fp32 cache: fp32 projections
+        WQ = torch.from_numpy(np.ascontiguousarray(wl.w.W_Q, dtype=np.float32)).cuda()
+        WK = torch.from_numpy(np.ascontiguousarray(wl.WK, dtype=np.float32)).cuda()
     x = torch.from_numpy(syn.x_new(cfg)).cuda()
     lens = torch.from_numpy(np.maximum(wl.lens - 1, 0).astype(np.int32)).cuda()
     nxt = torch.empty_like(lens)
-    ws = slim.workspace(slim.step_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max, slim.BF16))
+    ws = slim.workspace(slim.step_workspace_bytes(cfg.B, cfg.H, cfg.dh, cfg.T_max,
+                                                  slim.BF16 if cfg.cache == "bf16" else slim.F32))
     fn = lambda i: slim.step(x, WQ, WK, wl.K[i % len(wl.K)], lens, nxt, wl.W, wl.out, cfg.H, cfg.dh, cfg.scale, ws)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     return _loop_ms(torch, fn, steps)
+
+
+def step_record(wl, torch, slim, steps, ms_decode):
+    cfg = wl.cfg
+    ms_gen = time_step(wl, torch, slim, steps, 3)
+    wbytes = 2 * cfg.d * cfg.d * (2 if cfg.cache == "bf16" else 4)
+    rec = {"what": ("slim_step: q = x.W_Q and k = x.W_K (weights in the cache's precision, fp32 accumulate), "
+                    "attention over len_b - 1 cached rows, k appended at row len_b - 1"),
+           "tokens_s": cfg.B / (ms_gen * 1e-3), "ms_per_step": ms_gen,
+           "over_decode_us": (ms_gen - ms_decode) * 1e3, "projection_weight_bytes": wbytes}
+    log(f"[bench] {wl.name}: generation step {ms_gen * 1e3:.1f} us/step ({(ms_gen - ms_decode) * 1e3:.1f} us over "
+        f"the decode)")
+    return rec
 
 
 def _graph_ms(torch, fn, out, steps):
@@ -505,14 +528,7 @@ def main():
     }
 
     if extras:
-        ms_gen = time_step(wl, torch, slim, args.steps, 3)
-        res["generation_step"] = {
-            "what": ("slim_step: q = x.W_Q and k = x.W_K (bf16 weights, fp32 accumulate), attention "
-                     "over len_b - 1 cached rows, k appended at row len_b - 1"),
-            "tokens_s": cfg.B / (ms_gen * 1e-3), "ms_per_step": ms_gen,
-            "over_decode_us": (ms_gen - ms_step) * 1e3,
-            "projection_weight_bytes": 2 * cfg.d * cfg.d * 2}
-        log(f"[bench] generation step: {ms_gen * 1e3:.1f} us/step ({(ms_gen - ms_step) * 1e3:.1f} us over the decode)")
+        res["generation_step"] = step_record(wl, torch, slim, args.steps, ms_step)
         res["probe_read_gbps"] = probe_read_gbps(torch, slim, wl.K[0])
         log(f"[bench] HBM read probe: {res['probe_read_gbps']:.0f} GB/s")
         res["probe_copy_gbps"] = probe_copy_gbps(torch, slim, wl.K[1], wl.K[0])
@@ -529,6 +545,9 @@ def main():
             continue
         w2 = Workload(s, torch, slim, with_v=extras)
         res["shapes"][s] = decode_record(w2, torch, slim, args.steps, args.warmup, with_kv=extras)
+        if extras:
+            res["shapes"][s]["generation_step"] = step_record(w2, torch, slim, args.steps,
+                                                              res["shapes"][s]["ms_per_step"])
         del w2
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -20,6 +20,7 @@
 //           the cache format (round to nearest even for bf16) when
 //           len_b < T_max, and lengths_next[b] = len_b + 1 (T_max when full).
 #include "common.hpp"
+#include "mfma16.hpp"
 #include "step.hpp"
 
 namespace slim {
@@ -168,58 +169,71 @@ __global__ void __launch_bounds__(512) qk_proj_kernel(const float* __restrict__ 
 
 // Many sequences (B >= 8): the same product on MFMA.  x is fp32; it is
 // split into three bf16 parts x = hi + mid + lo (together they carry fp32's
-// 24 significant bits), each multiplied by bf16 W on 32x32x8 MFMA with fp32
+// 24 significant bits), each multiplied by bf16 W on 32x32x16 MFMA with fp32
 // accumulation, so every product is exact and only the accumulation rounds,
 // as on the vector path.  Workgroup: 32 sequences x 256 columns of [q | k]
 // (four waves of 64) x KR rows of W in 64-row blocks; the W block sits in LDS
-// row-major (transpose reads give the B operands), the x block as its three
-// bf16 parts (one 8-byte read per A operand).
+// row-major (two transpose reads give a B operand), the x block as its three
+// bf16 parts (one 16-byte read per A operand).  Blocks are staged through
+// registers three deep into two LDS buffers (one barrier per block); every
+// load is issued with its indexes clamped, and rows past the workgroup's
+// range are zeroed when the block is put into LDS, so that the compiler's
+// wait counts leave the younger blocks in flight.
 constexpr int kQmCols = 256, kQmRows = 64;
 constexpr int kQmWPitch = kQmCols * 2 + 16;  // bytes per W row in LDS
-constexpr int kQmXPitch = kQmRows * 2 + 8;   // bytes per x row (one part) in LDS
+constexpr int kQmXPitch = kQmRows * 2 + 16;  // bytes per x row (one part) in LDS
+constexpr int kQmStages = 3;
+constexpr int kQmWBytes = kQmRows * kQmWPitch, kQmBuf = kQmWBytes + 3 * 32 * kQmXPitch;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_q;
 
 __global__ void __launch_bounds__(256) qk_mfma_kernel(const float* __restrict__ x, const uint16_t* __restrict__ WQ,
                                                       const uint16_t* __restrict__ WK, float* __restrict__ part,
                                                       int B, int d, int KR) {
-  __shared__ __attribute__((aligned(16))) char Ws[kQmRows * kQmWPitch];
-  __shared__ __attribute__((aligned(16))) char Xs[3 * 32 * kQmXPitch];
+  __shared__ __attribute__((aligned(16))) char lds[2 * kQmBuf];  // two buffers of [W rows | x parts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int n2 = 2 * d;
   const int c0 = blockIdx.x * kQmCols;
   const int k0 = blockIdx.y * KR, k1 = min(d, k0 + KR);
   const int b0 = blockIdx.z * 32;
+  const int nkb = (k1 - k0 + kQmRows - 1) / kQmRows;
 
   // staging: 8 chunks of W (row c/32, 8 columns at 8*(c%32)) and 8 x values
-  uint4 sw[8];
-  float sx[8];
-  auto load = [&](int kb) {
+  // (sequence c/64, row c%64); clamped sequences only feed outputs that are
+  // not stored
+  struct Stage {
+    uint4 w[8];
+    float x[8];
+  };
+  Stage st[kQmStages];
+  auto load = [&](Stage& g, int kb) {
+    const int kr = k0 + kb * kQmRows;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
-      const int r = c >> 5, col = c0 + (c & 31) * 8;
-      sw[i] = make_uint4(0, 0, 0, 0);
-      if (kb + r < k1 && col < n2) {
-        const uint16_t* Wm = col < d ? WQ : WK;
-        sw[i] = *reinterpret_cast<const uint4*>(Wm + (size_t)(kb + r) * d + (col < d ? col : col - d));
-      }
-      const int xb = c >> 6, xk = c & 63;  // 32 sequences x 64 rows
-      sx[i] = (b0 + xb < B && kb + xk < k1) ? x[(size_t)(b0 + xb) * d + kb + xk] : 0.f;
+      const int r = min(kr + (c >> 5), d - 1), col = min(c0 + (c & 31) * 8, n2 - 8);
+      const uint16_t* Wm = col < d ? WQ : WK;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Wm + (size_t)r * d + (col < d ? col : col - d));
+      g.w[i] = make_uint4(v.x, v.y, v.z, v.w);
+      const int xb = min(b0 + (c >> 6), B - 1), xk = min(kr + (c & 63), d - 1);
+      g.x[i] = x[(size_t)xb * d + xk];
     }
   };
-  auto store = [&]() {
+  auto store = [&](const Stage& g, char* buf, int kb) {
+    const int kr = k0 + kb * kQmRows;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(Ws + (c >> 5) * kQmWPitch + (c & 31) * 16) = sw[i];
+      const bool wok = kr + (c >> 5) < k1;
+      *reinterpret_cast<uint4*>(buf + (c >> 5) * kQmWPitch + (c & 31) * 16) =
+          make_uint4(wok ? g.w[i].x : 0u, wok ? g.w[i].y : 0u, wok ? g.w[i].z : 0u, wok ? g.w[i].w : 0u);
       const int xb = c >> 6, xk = c & 63;
-      const float v = sx[i];
+      const float v = kr + xk < k1 ? g.x[i] : 0.f;
       const uint32_t hi = f32_to_bf16_rne(v);
       const float r1 = v - __uint_as_float(hi << 16);
       const uint32_t mid = f32_to_bf16_rne(r1);
       const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
-      char* px = Xs + xb * kQmXPitch + xk * 2;
+      char* px = buf + kQmWBytes + xb * kQmXPitch + xk * 2;
       *reinterpret_cast<uint16_t*>(px) = (uint16_t)hi;
       *reinterpret_cast<uint16_t*>(px + 32 * kQmXPitch) = (uint16_t)mid;
       *reinterpret_cast<uint16_t*>(px + 64 * kQmXPitch) = (uint16_t)lo;
@@ -227,35 +241,48 @@ __global__ void __launch_bounds__(256) qk_mfma_kernel(const float* __restrict__ 
   };
 
   f32x16 acc[2] = {f32x16{0}, f32x16{0}};
-  // A operands: sequence lane%32, rows 8*kk + 4*h .. +3 of each part
-  const char* xa = Xs + (lane & 31) * kQmXPitch + h * 8;
-  // B operands by transpose read (as in the prefill GEMM): lane L points at
-  // columns 16*((L/16)%2) + 4*(L%4) of W row 4*(L/32) + (L%16)/4 of a
-  // 32-column tile and an 8-row step
-  const uint32_t wb = (uint32_t)(uintptr_t)Ws + (uint32_t)((4 * h + ((lane & 15) >> 2)) * kQmWPitch +
-                                                           (wave * 64 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
-  load(k0);
-  for (int kb = k0; kb < k1; kb += kQmRows) {
-    store();
+  // A operands: sequence lane%32, rows 16*kk + 8*h .. +7 of each part
+  const uint32_t xa = (uint32_t)(kQmWBytes + (lane & 31) * kQmXPitch + h * 16);
+  // B operands by two transpose reads (as in the prefill GEMM): lane L
+  // points at columns 16*((L/16)%2) + 4*(L%4) of W row 8*(L/32) + (L%16)/4
+  // of a 32-column tile and a 16-row step, and 4 rows further down
+  const uint32_t wb = (uint32_t)((8 * h + ((lane & 15) >> 2)) * kQmWPitch +
+                                 (wave * 64 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+  auto block = [&](int kb, Stage& g) {
+    char* buf = lds + (kb & 1) * kQmBuf;
+    store(g, buf, kb);
     __syncthreads();
-    if (kb + kQmRows < k1) load(kb + kQmRows);
+    load(g, min(kb + kQmStages, nkb - 1));
+    const uint32_t base = (uint32_t)(uintptr_t)buf;
 #pragma unroll
-    for (int kk = 0; kk < kQmRows / 8; ++kk) {
-      s16x4 a[3], bo[2];
+    for (int kk = 0; kk < kQmRows / 16; ++kk) {
+      bf16x8_t a[3], bo[2];
 #pragma unroll
-      for (int p3 = 0; p3 < 3; ++p3) a[p3] = *reinterpret_cast<const s16x4*>(xa + p3 * 32 * kQmXPitch + 16 * kk);
+      for (int p3 = 0; p3 < 3; ++p3)
+        a[p3] = *reinterpret_cast<const bf16x8_t*>(buf + xa + p3 * 32 * kQmXPitch + 32 * kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t o = base + wb + (uint32_t)(16 * kk * kQmWPitch + 64 * j);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_q*)(size_t)o);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_q*)(size_t)(o + 4 * kQmWPitch));
+        bo[j] = join_bf16x8(lo, hi);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bo[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_q*)(size_t)(wb + (uint32_t)(8 * kk * kQmWPitch + 64 * j)));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int p3 = 0; p3 < 3; ++p3)
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a[p3], bo[j], acc[j], 0, 0, 0);
+        for (int p3 = 0; p3 < 3; ++p3) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[p3], bo[j], acc[j], 0, 0, 0);
     }
-    __syncthreads();
+  };
+#pragma unroll
+  for (int j = 0; j < kQmStages; ++j) load(st[j], min(j, nkb - 1));
+  const int nfull = nkb / kQmStages * kQmStages;
+  for (int kb = 0; kb < nfull; kb += kQmStages) {
+#pragma unroll
+    for (int j = 0; j < kQmStages; ++j) block(kb + j, st[j]);
   }
+#pragma unroll
+  for (int j = 0; j < kQmStages - 1; ++j)
+    if (nfull + j < nkb) block(nfull + j, st[j]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = c0 + wave * 64 + 32 * j + (lane & 31);
