@@ -124,6 +124,36 @@ def test_prefill_bf16_matches_oracle():
     check_prefill_bf16(bf16_bits(Kd), oracle.bf16_decode(Xb), oracle.bf16_decode(Wb), "whisper_large-shape")
 
 
+@pytest.mark.parametrize("B,n,d", [(3, 37, 72), (2, 70, 200), (1, 300, 1032)])
+def test_prefill_bf16_ragged_tiles(B, n, d):
+    """bf16 prefill where the last k block, the last column tile and the last
+    row tile are all partial (d not a multiple of 64 or 128, B*n not a
+    multiple of 64), and the k-block count is not a multiple of the
+    prefetch depth; appended at row offsets with the rows past T_max
+    skipped."""
+    torch = pytest.importorskip("torch")
+    import kv_cache_reduction_amd as slim
+    rng = np.random.default_rng(d)
+    Xb = syn.f32_to_bf16_bits(rng.standard_normal((B, n, d)).astype(np.float32))
+    Wb = syn.f32_to_bf16_bits((rng.standard_normal((d, d)) / np.sqrt(d)).astype(np.float32))
+    T = n + 9
+    t0 = np.array([(5 * b) % 12 for b in range(B)], dtype=np.int32)
+    Kd = torch.zeros((B, T, d), dtype=torch.bfloat16, device="cuda")
+    slim.prefill(to_dev(Xb), to_dev(Wb), Kd, t0=to_dev(t0))
+    torch.cuda.synchronize()
+    bits = bf16_bits(Kd)
+    X64, W64 = oracle.bf16_decode(Xb), oracle.bf16_decode(Wb)
+    rows, xs = [], []
+    for b in range(B):
+        for i in range(n):
+            if t0[b] + i < T:
+                rows.append(bits[b, t0[b] + i])
+                xs.append(X64[b, i])
+        skipped = [t for t in range(T) if not (t0[b] <= t < t0[b] + n)]
+        assert np.all(bits[b, skipped] == 0)
+    check_prefill_bf16(np.array(rows), np.array(xs), W64, f"ragged tiles B={B} n={n} d={d}")
+
+
 def test_prefill_append_offsets_and_fp32():
     torch = pytest.importorskip("torch")
     import kv_cache_reduction_amd as slim
