@@ -124,13 +124,14 @@ def test_prefill_bf16_matches_oracle():
     check_prefill_bf16(bf16_bits(Kd), oracle.bf16_decode(Xb), oracle.bf16_decode(Wb), "whisper_large-shape")
 
 
-@pytest.mark.parametrize("B,n,d", [(3, 37, 72), (2, 70, 200), (1, 300, 1032)])
+@pytest.mark.parametrize("B,n,d", [(3, 37, 72), (2, 70, 200), (1, 300, 1032), (1, 1000, 4096)])
 def test_prefill_bf16_ragged_tiles(B, n, d):
     """bf16 prefill where the last k block, the last column tile and the last
     row tile are all partial (d not a multiple of 64 or 128, B*n not a
     multiple of 64), and the k-block count is not a multiple of the
     prefetch depth; appended at row offsets with the rows past T_max
-    skipped."""
+    skipped.  The shapes reach the 64x64 tiles and (1000 x 4096) the
+    64x128 ones."""
     torch = pytest.importorskip("torch")
     import kv_cache_reduction_amd as slim
     rng = np.random.default_rng(d)
