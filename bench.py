@@ -232,7 +232,7 @@ def decode_record(wl, torch, slim, steps, warmup, with_kv):
     ms_step, step, attend, finish = time_decode(wl, torch, slim, steps, warmup)
     gbps = wl.k_bytes / (ms_step * 1e-3) / 1e9
     att_gbps = wl.k_bytes / (attend["mean"] * 1e-6) / 1e9
-    rec = {"workload": cfg.desc, "B": cfg.B, "d": cfg.d, "H": cfg.H, "dh": cfg.dh, "T_max": cfg.T_max,
+    rec = {"workload": cfg.desc, "seed": cfg.seed, "B": cfg.B, "d": cfg.d, "H": cfg.H, "dh": cfg.dh, "T_max": cfg.T_max,
            "k_bytes": wl.k_bytes, "rotated_copies": len(wl.K),
            "tokens_s": cfg.B / (ms_step * 1e-3), "ms_per_step": ms_step,
            "k_cache_gbps": gbps, "k_cache_hbm_frac": gbps / HBM_PEAK_GBPS,
@@ -247,7 +247,9 @@ def decode_record(wl, torch, slim, steps, warmup, with_kv):
         ms_kv = time_kv(wl, torch, slim, steps, 3)
         rec["comparator"] = {"what": "standard MHA decode over explicit bf16 K and V caches (same box)",
                              "tokens_s": cfg.B / (ms_kv * 1e-3), "ms_per_step": ms_kv,
-                             "kv_gbps": 2 * wl.k_bytes / (ms_kv * 1e-3) / 1e9, "slim_speedup": ms_kv / ms_step}
+                             "kv_gbps": 2 * wl.k_bytes / (ms_kv * 1e-3) / 1e9, "slim_speedup": ms_kv / ms_step,
+                             # context memory of Slim (K only) against the comparator's K and V caches
+                             "cache_bytes_ratio": wl.K[0].numel() / (wl.K[0].numel() + wl.V[0].numel())}
         log(f"[bench] {wl.name}: comparator {ms_kv * 1e3:.1f} us/step, slim speedup {ms_kv / ms_step:.2f}x")
     return rec
 
@@ -530,6 +532,8 @@ def main():
     if extras:
         res["generation_step"] = step_record(wl, torch, slim, args.steps, ms_step)
         res["probe_read_gbps"] = probe_read_gbps(torch, slim, wl.K[0])
+        # the attend's rate against the streaming-read ceiling measured on the same box
+        res["decode"]["attend_frac_of_read_probe"] = head["attend_gbps"] / res["probe_read_gbps"]
         log(f"[bench] HBM read probe: {res['probe_read_gbps']:.0f} GB/s")
         res["probe_copy_gbps"] = probe_copy_gbps(torch, slim, wl.K[1], wl.K[0])
         log(f"[bench] HBM copy probe (read+write): {res['probe_copy_gbps']:.0f} GB/s")
@@ -545,6 +549,8 @@ def main():
             continue
         w2 = Workload(s, torch, slim, with_v=extras)
         res["shapes"][s] = decode_record(w2, torch, slim, args.steps, args.warmup, with_kv=extras)
+        if "probe_read_gbps" in res:
+            res["shapes"][s]["attend_frac_of_read_probe"] = res["shapes"][s]["attend_gbps"] / res["probe_read_gbps"]
         if extras:
             res["shapes"][s]["generation_step"] = step_record(w2, torch, slim, args.steps,
                                                               res["shapes"][s]["ms_per_step"])
