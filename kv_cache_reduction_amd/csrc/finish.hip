@@ -28,7 +28,8 @@
 //          accumulation rounds.  fp32 W_KV uses the vector ALU.
 //          The partials are read once and W_KV once per S sequences.
 // reduce   out[b, h, j] = sum_rb part[rb, b, h, j] in a fixed order, so the
-//          result does not depend on scheduling.
+//          result does not depend on scheduling (not launched when one row
+//          block covers d: merge_project then writes out itself).
 #include "common.hpp"
 #include "internal.hpp"
 #include "multi.hpp"
@@ -355,7 +356,8 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
   constexpr int RED = NSS * PR > NRS * DH ? NSS * PR : NRS * DH;
   const void* U = a.ws + pl.off_U;
   const float* ml = reinterpret_cast<const float*>(a.ws + pl.off_ml);
-  float* part = reinterpret_cast<float*>(a.ws + pl.off_op);
+  // one row block covering all of d (small d): the workgroups write out directly
+  float* part = pl.npc == 1 ? a.out : reinterpret_cast<float*>(a.ws + pl.off_op);
   const int spw = pl.spw == 16 ? 16 : 8;
   // MFMA projection when a workgroup has at least 4 sequences
   constexpr bool MFMA_OK = WBF16 && DH >= 16 && DH % 16 == 0;
@@ -380,7 +382,7 @@ static hipError_t launch_t(const DecodePlan& pl, const DecodeArgs& a, int fixed_
     hipLaunchKernelGGL((merge_project_kernel<DH, WBF16, PR, false, false>), grid, dim3(256), lds, s, a.lengths, U,
                        ml, a.W, part, a.status, a.B, a.H, a.d, a.T_max, pl.nch, pl.nslots, fixed_ns, spw);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pl.npc == 1) return e;
   const int n = a.B * a.H * DH;
   hipLaunchKernelGGL(proj_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, (const float*)part,
                      a.out, pl.npc, n);
