@@ -7,7 +7,8 @@
 //
 // multi_attend<DH, QW, OPT>  grid (column blocks, H x query groups, T splits),
 // QW waves of 64 lanes; wave w owns 32 queries of head h.
-//  * Tiles of 32 context rows travel global -> registers -> LDS (two tiles
+//  * Tiles of 64 context rows (32 for workgroups of fewer than four waves)
+//    travel global -> registers -> LDS (two tiles
 //    in flight in registers while a third is used from LDS; two LDS
 //    buffers, one barrier per tile): head h's DH key columns for the scores
 //    and the value block: 128 columns of K (option 2) or head h's DH columns
@@ -46,7 +47,7 @@ namespace slim {
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_m;
 
-constexpr int kMTile = 32;              // context rows per tile
+constexpr int kMRows = 32;              // context rows per score MFMA block (and the plan's split unit)
 constexpr float kMultiSlack = 8.f;      // log2 units
 constexpr uint32_t kOnes2 = 0x3f803f80u;  // two bf16 1.0
 
@@ -73,21 +74,27 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DH, int OPT>
+template <int DH, int QW, int OPT>
 struct MultiShape {
+  // score blocks per tile: two (64-row tiles) for four-wave workgroups,
+  // whose per-tile staging and barrier then cover twice the rows; one where
+  // the extra registers would not fit
+  static constexpr int MB = QW >= 4 ? 2 : 1;
+  static constexpr int MT = kMRows * MB;              // context rows per tile
   static constexpr int NCW = OPT == 2 ? 128 : DH;     // value columns per workgroup
   static constexpr int NCT = NCW / 32;                // 32-column MFMA tiles per wave
   static constexpr int SP = DH * 2 + 16;              // bytes per score row in LDS
   static constexpr int VP = NCW * 2 + 16;             // bytes per value row in LDS
-  static constexpr int SCH = kMTile * DH / 8;         // 16-byte chunks of the score part
-  static constexpr int VCH = kMTile * NCW / 8;        // 16-byte chunks of the value part
-  static constexpr int TILE = kMTile * (SP + VP);     // bytes per tile buffer
+  static constexpr int SCH = MT * DH / 8;             // 16-byte chunks of the score part
+  static constexpr int VCH = MT * NCW / 8;            // 16-byte chunks of the value part
+  static constexpr int TILE = MT * (SP + VP);         // bytes per tile buffer
 };
 
 template <int DH, int QW, int OPT>
 __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
-  using S = MultiShape<DH, OPT>;
+  using S = MultiShape<DH, QW, OPT>;
   constexpr int NT = 64 * QW;
+  constexpr int kMBlocks = S::MB, kMTile = S::MT;
   constexpr int CPT = (S::SCH + S::VCH + NT - 1) / NT;  // chunks per thread and tile
   extern __shared__ __attribute__((aligned(16))) char msm[];
   char* tiles = msm;                                               // [2][TILE]
@@ -208,35 +215,40 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     load_tile(st, tb + 2 * kMTile);
 
     // scores of the tile, transposed: S^T = K_h . Q_h^T with the K rows as
-    // the A operand and Q (registers) as the B operand.  The result layout
-    // leaves lane l with query l%32 at context rows 8k + 4*hh + j (register
-    // 4k + j), which is exactly the A-operand layout of P . V below.
-    f32x16 sc = f32x16{0};
-    {
-      const char* srow = buf + m * S::SP + hh * DH;  // context row l%32, this half's dimensions
+    // the A operand and Q (registers) as the B operand, one 32-row block at a
+    // time.  The result layout leaves lane l with query l%32 at context rows
+    // 32b + 8k + 4*hh + j (block b, register 4k + j), which is exactly the
+    // A-operand layout of P . V below.
+    float v[kMBlocks][16];
+#pragma unroll
+    for (int b = 0; b < kMBlocks; ++b) {
+      f32x16 sc = f32x16{0};
+      const char* srow = buf + (kMRows * b + m) * S::SP + hh * DH;  // context row, this half's dimensions
 #pragma unroll
       for (int k = 0; k < DH / 16; ++k) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(srow + 16 * k);
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qh[k], sc, 0, 0, 0);
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ql[k], sc, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[b][i] = sc[i];
     }
     // rows past a query's limit (or the split) are -inf; only tiles that
     // cross a limit of this wave need the per-element test
-    float v[16];
-    if (__builtin_amdgcn_ballot_w64(tb + kMTile > min(lim, t_end)) == 0) {
+    if (__builtin_amdgcn_ballot_w64(tb + kMTile > min(lim, t_end)) != 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = sc[i];
-    } else {
+      for (int b = 0; b < kMBlocks; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = 8 * (i >> 2) + 4 * hh + (i & 3);
-        v[i] = (tb + t < min(lim, t_end)) ? sc[i] : kNegInf;
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int t = kMRows * b + 8 * (i >> 2) + 4 * hh + (i & 3);
+          v[b][i] = (tb + t < min(lim, t_end)) ? v[b][i] : kNegInf;
+        }
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, v[i]);
+    for (int b = 0; b < kMBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, v[b][i]);
     mx = pair_max(mx);
     const bool up = mx > m_ref + kMultiSlack;
     if (__builtin_amdgcn_ballot_w64(up)) {  // some row moves its reference: rescale through LDS
@@ -256,19 +268,21 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     // summed from the same rounded weights the MFMA uses; m is finite once
     // any score of the row was, masked scores give 0 either way
     const float mu = fmaxf(m_ref, -__FLT_MAX__);
-    s16x4 pa[4];
+    s16x4 pa[kMBlocks][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const bf16x2_t p01 = {(__bf16)fast_exp2(v[4 * k] - mu), (__bf16)fast_exp2(v[4 * k + 1] - mu)};
-      const bf16x2_t p23 = {(__bf16)fast_exp2(v[4 * k + 2] - mu), (__bf16)fast_exp2(v[4 * k + 3] - mu)};
-      const uint32_t w0 = __builtin_bit_cast(uint32_t, p01), w1 = __builtin_bit_cast(uint32_t, p23);
-      l_half = dot2_bf16(w1, kOnes2, dot2_bf16(w0, kOnes2, l_half));
-      pa[k] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
-    }
+    for (int b = 0; b < kMBlocks; ++b)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2_t p01 = {(__bf16)fast_exp2(v[b][4 * k] - mu), (__bf16)fast_exp2(v[b][4 * k + 1] - mu)};
+        const bf16x2_t p23 = {(__bf16)fast_exp2(v[b][4 * k + 2] - mu), (__bf16)fast_exp2(v[b][4 * k + 3] - mu)};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, p01), w1 = __builtin_bit_cast(uint32_t, p23);
+        l_half = dot2_bf16(w1, kOnes2, dot2_bf16(w0, kOnes2, l_half));
+        pa[b][k] = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
+      }
     // P . value block, 16 context rows per MFMA
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const bf16x8_t a = join_bf16x8(pa[2 * k], pa[2 * k + 1]);
+    for (int k = 0; k < 2 * kMBlocks; ++k) {
+      const bf16x8_t a = join_bf16x8(pa[k >> 1][2 * (k & 1)], pa[k >> 1][2 * (k & 1) + 1]);
       const lds_s16x4_m* r0 =
           (const lds_s16x4_m*)(size_t)((uint32_t)(uintptr_t)(buf + tr_off) + (uint32_t)(16 * k * S::VP));
       const lds_s16x4_m* r1 =
@@ -364,7 +378,7 @@ __global__ void __launch_bounds__(256) multi_merge_kernel(const float* __restric
 
 template <int DH, int QW, int OPT>
 static hipError_t launch_mq(const MultiPlan& pl, const MultiParams& mp, hipStream_t s) {
-  using S = MultiShape<DH, OPT>;
+  using S = MultiShape<DH, QW, OPT>;
   const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * 4 + 16;
   auto kern = multi_attend_kernel<DH, QW, OPT>;
   static std::atomic<int> granted[kMaxDevices];
@@ -402,9 +416,9 @@ bool make_multi_plan(int n, int H, int dh, int T, int method, bool w_bf16, int n
   const long long wgs = ncb * H * nqg;
   // split the context while the grid is below two workgroups per compute unit
   int nsplit = 1;
-  while (wgs * nsplit * 2 <= 2LL * ncu && (long long)nsplit * 2 * kMTile * 4 <= T) nsplit *= 2;
+  while (wgs * nsplit * 2 <= 2LL * ncu && (long long)nsplit * 2 * kMRows * 4 <= T) nsplit *= 2;
   p->nsplit = nsplit;
-  p->Ts = ((T + nsplit - 1) / nsplit + kMTile - 1) / kMTile * kMTile;
+  p->Ts = ((T + nsplit - 1) / nsplit + kMRows - 1) / kMRows * kMRows;
   p->nsplit = (T + p->Ts - 1) / p->Ts;
   size_t off = 0;
   auto take = [&](size_t b) {
