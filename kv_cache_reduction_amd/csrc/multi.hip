@@ -110,31 +110,25 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   const int q = (qg * QW + wave) * 32 + m;                 // this lane's query row
   const bool qok = q < p.n;
 
-  // query limits: this lane's row, and the workgroup maximum (tiles stop there)
-  int lim = 0;
-  if (qok) {
-    lim = p.limits ? p.limits[q] : p.T;
-    lim = lim < 0 ? 0 : (lim > p.T ? p.T : lim);
-  }
-  if (tid == 0) *lim_max = 0;
-  __syncthreads();
-  if (hh == 0 && lim > 0) atomicMax(lim_max, lim);
-  __syncthreads();
-  const int t_begin = split * p.Ts;
-  const int t_end = min(min(p.T, t_begin + p.Ts), *lim_max);
-  const int ntiles = t_end > t_begin ? (t_end - t_begin + kMTile - 1) / kMTile : 0;
-
-  // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
-  // order: step k takes dimensions hh*DH/2 + 4k .. +3
   bf16x8_t qh[DH / 16], ql[DH / 16];
+  int lim_raw;
   {
     const float* qr = p.Q + (size_t)(qok ? q : 0) * d + h * DH + hh * (DH / 2);
+    // all of the lane's q loads and its row limit first (the row is
+    // clamped, so they are unconditional and in flight together), then the
+    // splits; rows past n are zeroed
+    u32x4 raw[DH / 8];
+#pragma unroll
+    for (int i = 0; i < DH / 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(qr + 4 * i);
+    lim_raw = p.limits ? p.limits[qok ? q : 0] : p.T;
 #pragma unroll
     for (int k = 0; k < DH / 16; ++k) {
       s16x4 hv[2], lv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float4 v = qok ? *reinterpret_cast<const float4*>(qr + 8 * k + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const u32x4 r = raw[2 * k + e];
+        const float4 v = make_float4(qok ? __uint_as_float(r.x) : 0.f, qok ? __uint_as_float(r.y) : 0.f,
+                                     qok ? __uint_as_float(r.z) : 0.f, qok ? __uint_as_float(r.w) : 0.f);
         uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
         split_bf16(v.x * p.qscale, h0, l0);
         split_bf16(v.y * p.qscale, h1, l1);
@@ -148,6 +142,19 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
     }
   }
 
+  // query limits: this lane's row, and the workgroup maximum (tiles stop there)
+  int lim = 0;
+  if (qok) lim = lim_raw < 0 ? 0 : (lim_raw > p.T ? p.T : lim_raw);
+  if (tid == 0) *lim_max = 0;
+  __syncthreads();
+  if (hh == 0 && lim > 0) atomicMax(lim_max, lim);
+  __syncthreads();
+  const int t_begin = split * p.Ts;
+  const int t_end = min(min(p.T, t_begin + p.Ts), *lim_max);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kMTile - 1) / kMTile : 0;
+
+  // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
+  // order: step k takes dimensions hh*DH/2 + 4k .. +3
   // tile loads: chunk c < SCH is score row c / (DH/8), 8 columns at
   // 8*(c % (DH/8)); the rest are value rows.  Each thread's chunks are fixed,
   // so their sources (row 0 of the tile), rows and LDS offsets are computed
