@@ -18,12 +18,14 @@ constexpr float kNegInf = -__builtin_inff();
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).  Both results
+// are formed and one is selected, so that long unrolled runs of conversions
+// stay free of branches and exec-mask changes.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
 // Two fp32 -> one word of two bf16 (lo in bits 0..15).

@@ -99,7 +99,6 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   extern __shared__ __attribute__((aligned(16))) char msm[];
   char* tiles = msm;                                               // [2][TILE]
   float* rowv = reinterpret_cast<float*>(msm + 2 * S::TILE);       // [QW][32]
-  int* lim_max = reinterpret_cast<int*>(rowv + QW * 32);           // [1]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, m = lane & 31;
   const int nqg = (p.n + 32 * QW - 1) / (32 * QW);
@@ -110,51 +109,27 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   const int q = (qg * QW + wave) * 32 + m;                 // this lane's query row
   const bool qok = q < p.n;
 
-  bf16x8_t qh[DH / 16], ql[DH / 16];
-  int lim_raw;
+  const int t_begin = split * p.Ts;
+  const int q_first = qg * QW * 32;  // the workgroup's first query row
+
+  // every load of the set-up is issued first, in the order the data is
+  // needed, with clamped rows so that none sits under a branch and all are
+  // in flight together: the query limits, this lane's q row, then the first
+  // two context tiles
+  constexpr int kLimLoads = (QW * 32 + 63) / 64;
+  int lim_raw = p.T, wg_raw[kLimLoads];
+  if (p.limits) {
+    lim_raw = p.limits[qok ? q : 0];
+#pragma unroll
+    for (int i = 0; i < kLimLoads; ++i) wg_raw[i] = p.limits[min(q_first + 64 * i + lane, p.n - 1)];
+  }
+  u32x4 qraw[DH / 8];
   {
     const float* qr = p.Q + (size_t)(qok ? q : 0) * d + h * DH + hh * (DH / 2);
-    // all of the lane's q loads and its row limit first (the row is
-    // clamped, so they are unconditional and in flight together), then the
-    // splits; rows past n are zeroed
-    u32x4 raw[DH / 8];
 #pragma unroll
-    for (int i = 0; i < DH / 8; ++i) raw[i] = *reinterpret_cast<const u32x4*>(qr + 4 * i);
-    lim_raw = p.limits ? p.limits[qok ? q : 0] : p.T;
-#pragma unroll
-    for (int k = 0; k < DH / 16; ++k) {
-      s16x4 hv[2], lv[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const u32x4 r = raw[2 * k + e];
-        const float4 v = make_float4(qok ? __uint_as_float(r.x) : 0.f, qok ? __uint_as_float(r.y) : 0.f,
-                                     qok ? __uint_as_float(r.z) : 0.f, qok ? __uint_as_float(r.w) : 0.f);
-        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_bf16(v.x * p.qscale, h0, l0);
-        split_bf16(v.y * p.qscale, h1, l1);
-        split_bf16(v.z * p.qscale, h2, l2);
-        split_bf16(v.w * p.qscale, h3, l3);
-        hv[e] = s16x4{(short)h0, (short)h1, (short)h2, (short)h3};
-        lv[e] = s16x4{(short)l0, (short)l1, (short)l2, (short)l3};
-      }
-      qh[k] = join_bf16x8(hv[0], hv[1]);
-      ql[k] = join_bf16x8(lv[0], lv[1]);
-    }
+    for (int i = 0; i < DH / 8; ++i) qraw[i] = *reinterpret_cast<const u32x4*>(qr + 4 * i);
   }
 
-  // query limits: this lane's row, and the workgroup maximum (tiles stop there)
-  int lim = 0;
-  if (qok) lim = lim_raw < 0 ? 0 : (lim_raw > p.T ? p.T : lim_raw);
-  if (tid == 0) *lim_max = 0;
-  __syncthreads();
-  if (hh == 0 && lim > 0) atomicMax(lim_max, lim);
-  __syncthreads();
-  const int t_begin = split * p.Ts;
-  const int t_end = min(min(p.T, t_begin + p.Ts), *lim_max);
-  const int ntiles = t_end > t_begin ? (t_end - t_begin + kMTile - 1) / kMTile : 0;
-
-  // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
-  // order: step k takes dimensions hh*DH/2 + 4k .. +3
   // tile loads: chunk c < SCH is score row c / (DH/8), 8 columns at
   // 8*(c % (DH/8)); the rest are value rows.  Each thread's chunks are fixed,
   // so their sources (row 0 of the tile), rows and LDS offsets are computed
@@ -196,6 +171,50 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
       if (ch_ok[i]) *reinterpret_cast<uint4*>(buf + ch_lds[i]) = st[i];
   };
 
+  load_tile(stage[0], t_begin);
+  load_tile(stage[1], t_begin + kMTile);
+
+  // query limits: this lane's row (clamped to [0, T]), and the workgroup's
+  // largest, where its tiles stop; each wave reduces all of the workgroup's
+  // rows itself, so no barrier is needed
+  const auto clamp_t = [&](int x) { return x < 0 ? 0 : (x > p.T ? p.T : x); };
+  const int lim = qok ? clamp_t(lim_raw) : 0;
+  int wg_lim = p.T;
+  if (p.limits) {
+    wg_lim = 0;
+#pragma unroll
+    for (int i = 0; i < kLimLoads; ++i)
+      if (64 * i + lane < QW * 32 && q_first + 64 * i + lane < p.n) wg_lim = max(wg_lim, clamp_t(wg_raw[i]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wg_lim = max(wg_lim, __shfl_xor(wg_lim, off));
+    wg_lim = __builtin_amdgcn_readfirstlane(wg_lim);
+  }
+  const int t_end = min(min(p.T, t_begin + p.Ts), wg_lim);
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kMTile - 1) / kMTile : 0;
+
+  // Q_h of this lane's row, scaled, as bf16 hi/lo in the score A-operand
+  // order: step k takes dimensions hh*DH/2 + 4k .. +3; rows past n are zero
+  bf16x8_t qh[DH / 16], ql[DH / 16];
+#pragma unroll
+  for (int k = 0; k < DH / 16; ++k) {
+    s16x4 hv[2], lv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const u32x4 r = qraw[2 * k + e];
+      const float4 v = make_float4(qok ? __uint_as_float(r.x) : 0.f, qok ? __uint_as_float(r.y) : 0.f,
+                                   qok ? __uint_as_float(r.z) : 0.f, qok ? __uint_as_float(r.w) : 0.f);
+      uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+      split_bf16(v.x * p.qscale, h0, l0);
+      split_bf16(v.y * p.qscale, h1, l1);
+      split_bf16(v.z * p.qscale, h2, l2);
+      split_bf16(v.w * p.qscale, h3, l3);
+      hv[e] = s16x4{(short)h0, (short)h1, (short)h2, (short)h3};
+      lv[e] = s16x4{(short)l0, (short)l1, (short)l2, (short)l3};
+    }
+    qh[k] = join_bf16x8(hv[0], hv[1]);
+    ql[k] = join_bf16x8(lv[0], lv[1]);
+  }
+
   float* rv = rowv + wave * 32;
   // transpose-read offset of the value part: lane L reads 4 columns
   // 32s + 16*((L/16)%2) + 4*(L%4) of row 8k + 4*(L/32) + (L%16)/4; the
@@ -209,10 +228,6 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
   for (int s = 0; s < S::NCT; ++s) acc[s] = f32x16{0};
   float m_ref = kNegInf, l_half = 0.f;
 
-  // loads are issued unconditionally (rows clamped), so that the compiler
-  // can count the tiles in flight and wait for one tile only
-  load_tile(stage[0], t_begin);
-  load_tile(stage[1], t_begin + kMTile);
   // one tile: into LDS from its stage, then the stage takes tile it + 2
   auto tile = [&](int it, uint4 (&st)[CPT]) {
     char* buf = tiles + (it & 1) * S::TILE;
@@ -386,7 +401,7 @@ __global__ void __launch_bounds__(256) multi_merge_kernel(const float* __restric
 template <int DH, int QW, int OPT>
 static hipError_t launch_mq(const MultiPlan& pl, const MultiParams& mp, hipStream_t s) {
   using S = MultiShape<DH, QW, OPT>;
-  const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * 4 + 16;
+  const size_t lds = 2 * (size_t)S::TILE + (size_t)QW * 32 * 4;
   auto kern = multi_attend_kernel<DH, QW, OPT>;
   static std::atomic<int> granted[kMaxDevices];
   const hipError_t e = allow_lds(reinterpret_cast<const void*>(kern), lds, granted);
