@@ -5,7 +5,8 @@
 // values follow from V = K.W_KV, either formed first (option 1) or applied
 // after the softmax has been multiplied by K (option 2).
 //
-// multi_attend<DH, QW, OPT>  grid (column blocks, H x query groups, T splits),
+// multi_attend<DH, QW, OPT>  grid (column blocks, H x query groups, T splits;
+// with row limits the query groups are taken heaviest first),
 // QW waves of 64 lanes; wave w owns 32 queries of head h.
 //  * Tiles of 64 context rows (32 for workgroups of fewer than four waves)
 //    travel global -> registers -> LDS (two tiles
@@ -102,8 +103,23 @@ __global__ void __launch_bounds__(64 * QW) multi_attend_kernel(MultiParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, m = lane & 31;
   const int nqg = (p.n + 32 * QW - 1) / (32 * QW);
-  const int h = blockIdx.y / nqg, qg = blockIdx.y - h * nqg;
-  const int split = blockIdx.z;
+  // (head, query group, split) of the workgroup.  With row limits (the
+  // causal prompt, where later queries see more rows) the workgroups are
+  // dispatched heaviest first: query groups in descending order, heads
+  // innermost, so that the light ones come last and share CUs with the
+  // others; any order is correct, this one shortens the tail.  Without
+  // limits every workgroup has the same work.
+  int h, qg, split;
+  if (p.limits) {
+    const int L = blockIdx.y + gridDim.y * blockIdx.z, rest = L / p.H;
+    h = L - rest * p.H;
+    qg = nqg - 1 - rest / p.nsplit;
+    split = rest - (rest / p.nsplit) * p.nsplit;
+  } else {
+    h = blockIdx.y / nqg;
+    qg = blockIdx.y - h * nqg;
+    split = blockIdx.z;
+  }
   const int d = p.d;
   const int c0 = OPT == 2 ? blockIdx.x * S::NCW : h * DH;  // first value column
   const int q = (qg * QW + wave) * 32 + m;                 // this lane's query row
