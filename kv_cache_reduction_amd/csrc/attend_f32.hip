@@ -33,6 +33,10 @@ struct AttendF32Params {
 
 constexpr int kF32MaxHeads = 64;
 
+// MAXH >= H bounds the per-thread head loops at compile time, so that the
+// accumulators stay in registers and a small H does not walk (and branch
+// over) all kF32MaxHeads of them.
+template <int MAXH>
 __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
   extern __shared__ int smem[];
   const int RB = p.rb;
@@ -65,9 +69,9 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
     for (int i = tid; i < p.d; i += 256) qs[i] = p.q[(size_t)b * p.d + i];
 
     float m = kNegInf, l = 0.f;  // head tid (tid < H)
-    float acc[kF32MaxHeads];
+    float acc[MAXH];
 #pragma unroll
-    for (int h = 0; h < kF32MaxHeads; ++h) acc[h] = 0.f;
+    for (int h = 0; h < MAXH; ++h) acc[h] = 0.f;
 
     for (int t0 = tb; t0 < te; t0 += RB) {
       const int nr = min(RB, te - t0);
@@ -98,7 +102,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
         for (int r = 0; r < nr; ++r) {
           const float kv = rows[(size_t)r * p.d + col];
 #pragma unroll
-          for (int h = 0; h < kF32MaxHeads; ++h)
+          for (int h = 0; h < MAXH; ++h)
             if (h < p.H) acc[h] = fmaf(sc[r * p.H + h], kv, al[r * p.H + h] * acc[h]);
         }
       }
@@ -106,7 +110,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
     }
     if (col_ok) {
 #pragma unroll
-      for (int h = 0; h < kF32MaxHeads; ++h)
+      for (int h = 0; h < MAXH; ++h)
         if (h < p.H) p.U[((size_t)h * p.nslots + slot) * p.d + col] = acc[h];
     }
     if (cb == 0 && tid < p.H) {
@@ -114,6 +118,15 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(AttendF32Params p) {
       p.ml[(size_t)slot * 2 * p.H + p.H + tid] = l;
     }
   }
+}
+
+template <int MAXH>
+static hipError_t launch_heads(const AttendF32Params& p, const DecodePlan& pl, size_t lds, hipStream_t s) {
+  static std::atomic<int> granted[kMaxDevices];
+  const hipError_t e = allow_lds(reinterpret_cast<const void*>(attend_f32_kernel<MAXH>), lds, granted);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_f32_kernel<MAXH>, dim3(pl.nch * pl.gc), dim3(256), lds, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStream_t s) {
@@ -140,11 +153,12 @@ hipError_t launch_attend_f32(const DecodePlan& pl, const DecodeArgs& a, hipStrea
   if (rb < 1) rb = 1;
   p.rb = rb;
   const size_t lds = (4 + (size_t)a.d + (size_t)rb * a.d + 2 * (size_t)rb * a.H + (size_t)a.B + 1) * 4;
-  static std::atomic<int> granted[kMaxDevices];
-  const hipError_t e = allow_lds(reinterpret_cast<const void*>(attend_f32_kernel), lds, granted);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_f32_kernel, dim3(pl.nch * pl.gc), dim3(256), lds, s, p);
-  return hipGetLastError();
+  if (a.H <= 4) return launch_heads<4>(p, pl, lds, s);
+  if (a.H <= 8) return launch_heads<8>(p, pl, lds, s);
+  if (a.H <= 16) return launch_heads<16>(p, pl, lds, s);
+  if (a.H <= 32) return launch_heads<32>(p, pl, lds, s);
+  if (a.H <= kF32MaxHeads) return launch_heads<kF32MaxHeads>(p, pl, lds, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace slim
