@@ -67,6 +67,26 @@ def test_random_decode_fp32(seed):
     assert np.isfinite(o).all() and err <= TOL["f32"]
 
 
+@pytest.mark.parametrize("H", [1, 4, 5, 8, 9, 16, 17, 32, 33, 64])
+def test_decode_fp32_head_bucket_edges(H):
+    """The fp32 attend kernel is compiled for at most 4, 8, 16, 32 or 64
+    heads; head counts on both sides of each bound."""
+    rng = np.random.default_rng(5000 + H)
+    cfg = syn.Config("f32-heads", d=H * 16, H=H, dh=16, B=3, T_max=70, len_lo=0, len_hi=70,
+                     cache="f32", wkv="f32", seed=7000 + H)
+    wl = syn.make(syn.shrink(cfg, len_lo=cfg.T_max, len_hi=cfg.T_max), with_cache=False)
+    lens = _lengths(rng, cfg.B, cfg.T_max)
+    K = syn.k_cache(cfg, wl.w, np.minimum(lens, cfg.T_max))
+    log(f"[random] f32 heads: B={cfg.B} H={H} dh=16 T={cfg.T_max} lens={lens.tolist()}")
+    Wd = to_dev(__import__("kv_cache_reduction_amd").wkv(wl.w.W_K, wl.w.W_V, "f32"))
+    o = gpu_decode(cfg, wl.q, to_dev(K), lens, Wd)
+    ref = oracle_decode(cfg, wl.q, K, lens, wl.w.W_K, wl.w.W_V)
+    err = oracle.err_rel(o, ref)
+    log(f"[random] err={err:.3e}")
+    assert np.isfinite(o).all() and err <= TOL["f32"]
+    assert np.all(o[np.minimum(lens, cfg.T_max) == 0] == 0)
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_random_multi_query(seed):
     import torch
